@@ -1,0 +1,63 @@
+"""Plant plausible slips in a copy of the oracle (on the CPU) and check that
+the pins in ``test_oracle_pins.py`` catch every one of them."""
+import subprocess
+
+import pytest
+
+from oracle import oracle
+
+from . import test_oracle_pins as pins
+
+SRC = (oracle._SRC).read_text()
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("scale dropped", "const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0;"),
+    ("scale 1/D", "const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0 / (double)D;"),
+    ("q head -> wrong kv head", "g = h / G;", "g = h % p->Hkv;"),
+    ("slot within page off by one", "return page * page_size + t % page_size;",
+     "return page * page_size + (t + 1) % page_size;"),
+    ("page index ignores position", "page_table[b * max_pages + t / page_size]", "page_table[b * max_pages]"),
+    ("score sign", "double s = scale * dot;", "double s = -scale * dot;"),
+    ("V read from K pool", "const uint16_t *v = p->v_pool", "const uint16_t *v = p->k_pool"),
+    ("weights not normalised", "double wt = exp(scores[t - t0] - m) / denom;",
+     "double wt = exp(scores[t - t0] - m);"),
+    ("lse misses the max", "*lse = m + log(denom);", "*lse = log(denom);"),
+    ("merge weight inverted", "double ws = exp(lr[s] - M);", "double ws = exp(M - lr[s]);"),
+    ("merge not normalised", "o[d] /= den;", "o[d] /= 1.0;"),
+    ("merge lse misses the max", "lse[r] = M + log(den);", "lse[r] = log(den);"),
+    ("store copies the wrong row", "k_new + i * in_row_stride", "k_new + (n - 1 - i) * in_row_stride"),
+    ("store skips V", "memcpy(v_pool + slot * pool_row_stride", "if (0) memcpy(v_pool + slot * pool_row_stride"),
+    ("split end off by one", "if (t1 > seq_lens[b]) t1 = seq_lens[b];",
+     "if (t1 > seq_lens[b]) t1 = seq_lens[b] - 1;"),
+    ("bf16 widened wrongly", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    ("chunk not page aligned", "return (per + page_size - 1) / page_size * page_size;", "return per;"),
+]
+
+PIN_CALLS = [
+    (pins.test_store_selfcheck_shapes_match_index_put, ()),
+    (pins.test_store_of_generated_step_restores_the_drawn_pool, ()),
+    (pins.test_softmax_weights_sum_to_one, ()),
+    (pins.test_length_one_returns_that_value_row, ()),
+    (pins.test_identical_keys_give_mean_of_values, ()),
+    (pins.test_merge_closed_forms, ()),
+    (pins.test_split_chunk_reading, ()),
+    (pins.test_split_then_merge_equals_unsplit, (3,)),
+] + [(pins.test_attention_matches_torch_sdpa_fp64, (c,)) for c in range(4)]
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, orig, mut):
+    assert SRC.count(orig) >= 1, f"mutation site for '{name}' not found"
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.replace(orig, mut))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, "-w", str(src), "-o", str(lib), "-lm"], check=True)
+    caught = []
+    with oracle.use_library(lib):
+        for fn, args in PIN_CALLS:
+            try:
+                fn(*args)
+            except (AssertionError, ValueError):
+                caught.append(fn.__name__)
+    assert caught, f"no pin caught the mutant '{name}'"

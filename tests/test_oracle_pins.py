@@ -1,0 +1,300 @@
+"""Pins of the CPU oracle to things other than itself (no GPU).
+
+Each test checks the oracle against a library routine, a closed form, an
+invariant the mathematics fixes, or a figure the pages print.  Together they
+are chosen so that a plausible slip in the oracle (dropped scale, wrong kv-head
+for a q head, off-by-one in the page translation, a sign, a transposed operand,
+a wrong merge weight) fails at least one of them; ``test_oracle_mutants.py``
+plants such slips and checks exactly that.
+"""
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from paged_kv_gqa_store_amd import workloads as W
+
+GOLDEN = Path(__file__).parent / "golden"
+
+
+def _f64(bits):
+    return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def small_cases():
+    """Tiny shapes spanning G in {1,2,4,8}, D in {64,128}, page sizes 1..16, ragged lengths."""
+    yield W.CONFIGS[1], None
+    yield W.custom_config(name="g8_d128_p4", B=3, Hq=16, Hkv=2, D=128, P=4, num_pages=64,
+                          seq_lens=(1, 23, 50)), None
+    yield W.custom_config(name="mha_p1", B=2, Hq=3, Hkv=3, D=64, P=1, num_pages=200,
+                          seq_lens=(17, 64)), None
+    yield W.custom_config(name="g2_p8", B=2, Hq=4, Hkv=2, D=64, P=8, num_pages=40,
+                          seq_lens=(100, 9)), None
+
+
+# ---------------------------------------------------------------- store ----
+
+def _selfcheck_case(pool_slots, rows, row_bytes, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    kc = rng.integers(0, 256, (pool_slots, row_bytes), dtype=np.uint8)
+    vc = rng.integers(0, 256, (pool_slots, row_bytes), dtype=np.uint8)
+    k = rng.integers(0, 256, (rows, row_bytes), dtype=np.uint8)
+    v = rng.integers(0, 256, (rows, row_bytes), dtype=np.uint8)
+    idx = rng.permutation(pool_slots)[:rows].astype(np.int32)   # distinct destinations
+    return kc, vc, k, v, idx
+
+
+def test_store_selfcheck_shapes_match_index_put():
+    """The page's two self-check shapes; reference = torch's CPU index_put."""
+    cases = json.loads((GOLDEN / "store_selfcheck_shapes.json").read_text())["cases"]
+    for i, c in enumerate(cases):
+        kc, vc, k, v, idx = _selfcheck_case(c["pool_slots"], c["rows"], c["row_bytes"], 100 + i)
+        ko, vo = oracle.kv_store(kc, vc, k, v, idx)
+        tk = torch.from_numpy(kc.copy())
+        tv = torch.from_numpy(vc.copy())
+        tk.index_put_((torch.from_numpy(idx.astype(np.int64)),), torch.from_numpy(k))
+        tv.index_put_((torch.from_numpy(idx.astype(np.int64)),), torch.from_numpy(v))
+        assert ko.tobytes() == tk.numpy().tobytes(), c["name"]
+        assert vo.tobytes() == tv.numpy().tobytes(), c["name"]
+        untouched = np.setdiff1d(np.arange(c["pool_slots"]), idx)
+        assert (ko[untouched] == kc[untouched]).all() and (vo[untouched] == vc[untouched]).all()
+        assert (kc == _selfcheck_case(c["pool_slots"], c["rows"], c["row_bytes"], 100 + i)[0]).all()
+
+
+def test_store_partial_rows_and_strides():
+    """row_elems shorter than both strides: only the row prefix moves."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    pool = rng.integers(0, 1 << 16, (50, 40), dtype=np.uint16)
+    new = rng.integers(0, 1 << 16, (7, 33), dtype=np.uint16)
+    idx = rng.permutation(50)[:7].astype(np.int32)
+    ko, vo = oracle.kv_store(pool, pool, new, new, idx, row_elems=24)
+    exp = pool.copy()
+    exp[idx, :24] = new[:, :24]
+    assert (ko == exp).all() and (vo == exp).all()
+
+
+def test_store_rejects_out_of_range_slot():
+    pool = np.zeros((4, 8), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.kv_store(pool, pool, np.zeros((1, 8), np.uint16), np.zeros((1, 8), np.uint16),
+                        np.array([4], np.int32))
+
+
+def test_store_of_generated_step_restores_the_drawn_pool():
+    """Storing the step's rows over the canaries gives back the drawn pool."""
+    inp = W.make_inputs(W.CONFIGS[1])
+    cfg = inp.cfg
+    flat = lambda a: a.reshape(cfg.num_pages * cfg.P, cfg.row_elems)
+    ko, vo = oracle.kv_store(flat(inp.k_pool), flat(inp.v_pool), inp.k_new, inp.v_new, inp.slot_mapping)
+    kf, vf = inp.pools_after_store()
+    assert ko.tobytes() == flat(kf).tobytes() and vo.tobytes() == flat(vf).tobytes()
+
+
+# ------------------------------------------------------------ attention ----
+
+def _after_store(inp):
+    return inp.pools_after_store()
+
+
+def _gathered(inp, b):
+    """K and V rows of sequence b in position order, by torch advanced indexing."""
+    kf, vf = _after_store(inp)
+    cfg = inp.cfg
+    L = int(inp.seq_lens[b])
+    t = torch.arange(L)
+    pages = torch.from_numpy(inp.page_table[b].astype(np.int64))[t // cfg.P]
+    K = torch.from_numpy(_f64(kf))[pages, t % cfg.P]   # [L, Hkv, D]
+    V = torch.from_numpy(_f64(vf))[pages, t % cfg.P]
+    return K, V
+
+
+@pytest.mark.parametrize("case", list(range(4)))
+def test_attention_matches_torch_sdpa_fp64(case):
+    """Brute force on tiny inputs: torch float64 scaled_dot_product_attention
+    (default scale 1/sqrt(D)) with each kv head repeated over its q-head group."""
+    cfg, _ = list(small_cases())[case]
+    inp = W.make_inputs(cfg)
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    G = cfg.Hq // cfg.Hkv
+    for b in range(cfg.B):
+        K, V = _gathered(inp, b)
+        Kh = K.permute(1, 0, 2).repeat_interleave(G, dim=0)   # [Hq, L, D]
+        Vh = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
+        qb = torch.from_numpy(_f64(inp.q[b])).unsqueeze(1)    # [Hq, 1, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qb, Kh, Vh).squeeze(1)
+        np.testing.assert_allclose(out[b], ref.numpy(), rtol=0, atol=1e-12)
+        scores = torch.matmul(qb, Kh.transpose(1, 2).contiguous()).squeeze(1) / math.sqrt(cfg.D)
+        np.testing.assert_allclose(lse[b], torch.logsumexp(scores, dim=-1).numpy(), rtol=1e-14, atol=1e-12)
+
+
+def test_softmax_weights_sum_to_one():
+    inp = W.make_inputs(W.CONFIGS[1])
+    kf, vf = _after_store(inp)
+    for b in range(2):
+        for h in range(4):
+            w = oracle.softmax_weights(inp.q, kf, vf, inp.page_table, inp.seq_lens, b, h)
+            assert w.shape == (inp.seq_lens[b],)
+            assert (w >= 0).all()
+            assert abs(w.sum() - 1.0) <= 1e-12
+
+
+def test_length_one_returns_that_value_row():
+    cfg = W.custom_config(B=3, Hq=8, Hkv=2, D=128, P=16, num_pages=8, seq_lens=(1, 1, 1))
+    inp = W.make_inputs(cfg)
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    for b in range(3):
+        page = inp.page_table[b, 0]
+        for h in range(8):
+            g = h // 4
+            assert (out[b, h] == _f64(vf[page, 0, g])).all()
+            s = float(np.dot(_f64(inp.q[b, h]), _f64(kf[page, 0, g]))) / math.sqrt(128)
+            assert abs(lse[b, h] - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_identical_keys_give_mean_of_values():
+    cfg = W.custom_config(B=2, Hq=4, Hkv=2, D=64, P=4, num_pages=40, seq_lens=(13, 64))
+    inp = W.make_inputs(cfg)
+    kf, vf = _after_store(inp)
+    kf = kf.copy()
+    kf[:] = kf[inp.page_table[0, 0], 0]          # every slot holds one key row
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    for b in range(2):
+        _, V = _gathered(inp, b)
+        for h in range(4):
+            g = h // 2
+            mean = V[:, g].numpy().mean(axis=0)
+            np.testing.assert_allclose(out[b, h], mean, rtol=0, atol=1e-14)
+            s = float(np.dot(_f64(inp.q[b, h]), _f64(kf[0, 0, g]))) / 8.0
+            assert abs(lse[b, h] - (s + math.log(int(inp.seq_lens[b])))) <= 1e-12
+
+
+@pytest.mark.parametrize("case", list(range(4)))
+def test_paged_equals_contiguous_bitwise(case):
+    """Placement does not matter: the permuted pool and a contiguous
+    re-layout of the same sequences give bit-identical results."""
+    cfg, _ = list(small_cases())[case]
+    inp = W.make_inputs(cfg)
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    kc, vc, ptc = W.contiguous_layout(inp)
+    out2, lse2 = oracle.paged_decode(inp.q, kc, vc, ptc, inp.seq_lens)
+    assert out.tobytes() == out2.tobytes() and lse.tobytes() == lse2.tobytes()
+    # and a second, unrelated permutation of the same sequences
+    other = W.make_inputs(cfg, seed=inp.seed + 99)
+    assert not np.array_equal(other.page_table, inp.page_table) or cfg.B * cfg.num_pages < 4
+
+
+def test_rows_mode_equals_full_mode():
+    inp = W.make_inputs(W.CONFIGS[1])
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    rows = np.array([[1, 3], [0, 0], [1, 0]])
+    o2, l2 = oracle.paged_decode_rows(inp.q, kf, vf, inp.page_table, inp.seq_lens, rows)
+    for i, (b, h) in enumerate(rows):
+        assert (o2[i] == out[b, h]).all() and l2[i] == lse[b, h]
+
+
+def test_value_scaling_by_power_of_two_is_exact():
+    """Scaling V by 2^k scales the output by exactly 2^k."""
+    inp = W.make_inputs(W.CONFIGS[1])
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    v32 = W.bf16_bits_to_f32(vf)
+    fin = np.isfinite(v32)
+    v_scaled = vf.copy()
+    v_scaled[fin] = W.to_bf16_bits(v32[fin] * np.float32(2.0 ** 7))
+    out2, lse2 = oracle.paged_decode(inp.q, kf, v_scaled, inp.page_table, inp.seq_lens)
+    assert (out2 == out * 2.0 ** 7).all() and (lse2 == lse).all()
+
+
+def test_canaries_reach_the_output_when_the_store_is_skipped():
+    """Before the store, the new-token slot holds NaN: attention must see it."""
+    inp = W.make_inputs(W.CONFIGS[1])
+    out, _ = oracle.paged_decode(inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens)
+    assert np.isnan(out).all()
+    kf, vf = _after_store(inp)
+    out, _ = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    assert np.isfinite(out).all()
+
+
+def test_empty_sequence_gives_zero_and_minus_inf():
+    cfg = W.custom_config(B=2, Hq=2, Hkv=1, D=64, P=16, num_pages=4, seq_lens=(0, 5))
+    inp = W.make_inputs(cfg)
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+    assert np.isfinite(out[1]).all()
+
+
+# --------------------------------------------------------- split + merge ----
+
+def test_split_chunk_reading():
+    for L in [1, 15, 16, 17, 100, 4096, 65536, 8191]:
+        for S in [1, 2, 3, 4, 7, 32]:
+            for P in [1, 4, 16]:
+                c = oracle.split_chunk(L, S, P)
+                assert c % P == 0 and c * S >= L
+                assert c - P < -(-L // S)          # smallest page multiple >= ceil(L/S)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8])
+def test_split_then_merge_equals_unsplit(S):
+    inp = W.make_inputs(W.CONFIGS[1])
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    chunk = oracle.split_chunk(inp.max_seq_len, S, inp.cfg.P)
+    o_p, l_p = oracle.paged_decode_split(inp.q, kf, vf, inp.page_table, inp.seq_lens, chunk, S)
+    out2, lse2 = oracle.merge(o_p, l_p)
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-14, atol=1e-13)
+    # a split past a sequence's end is empty
+    for b in range(inp.cfg.B):
+        for s in range(S):
+            if s * chunk >= inp.seq_lens[b]:
+                assert np.isneginf(l_p[b, :, s]).all() and (o_p[b, :, s] == 0).all()
+
+
+def test_merge_closed_forms():
+    rng = np.random.Generator(np.random.PCG64(3))
+    o = rng.standard_normal((5, 2, 16))
+    # equal lse: the mean of the two partials, lse + ln 2
+    out, lse = oracle.merge(o, np.full((5, 2), 0.75))
+    np.testing.assert_allclose(out, o.mean(axis=1), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, 0.75 + math.log(2.0), rtol=0, atol=1e-15)
+    # lse differing by ln 3: weights 3/4 and 1/4
+    out, lse = oracle.merge(o, np.stack([np.full(5, math.log(3.0)), np.zeros(5)], 1))
+    np.testing.assert_allclose(out, 0.75 * o[:, 0] + 0.25 * o[:, 1], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, np.log(4.0), rtol=0, atol=1e-15)
+    # empty partials carry no weight; all empty gives 0 and -inf
+    o3 = np.concatenate([np.zeros((5, 1, 16)), o[:, :1], np.zeros((5, 1, 16))], axis=1)
+    l3 = np.stack([np.full(5, -np.inf), np.full(5, 2.5), np.full(5, -np.inf)], 1)
+    out, lse = oracle.merge(o3, l3)
+    assert (out == o[:, 0]).all() and (lse == 2.5).all()
+    out, lse = oracle.merge(np.zeros((2, 3, 4)), np.full((2, 3), -np.inf))
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+# ------------------------------------------------- measurement arithmetic ----
+
+def test_byte_accounting_reproduces_the_store_exercise():
+    g = json.loads((GOLDEN / "store_traffic_exercise.json").read_text())
+    row = g["kv_heads"] * g["head_dim"] * g["elem_bytes"]
+    assert row == g["row_bytes"]
+    assert 2 * g["batch_rows"] * row == g["kv_written_bytes"]
+    total = W.store_bytes(g["batch_rows"], row)
+    assert abs(total - g["traffic_bytes_approx"]) / g["traffic_bytes_approx"] < 0.01
+    us = W.roofline_us(total, g["bandwidth_bytes_per_s"])
+    assert abs(us - g["time_us_approx"]) < 0.01
+
+
+def test_kv_bytes_of_the_five_workloads():
+    assert W.kv_bytes([4096] * 32, 8, 128) == 536_870_912
+    assert W.kv_bytes([65536] * 4, 8, 128) == 1_073_741_824
+    assert W.kv_bytes([2048] * 128, 16, 64) == 1_073_741_824
+    assert W.kv_bytes([37, 100], 1, 64) == 35_072
