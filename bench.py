@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of GQA over a paged KV cache on one MI355X.
+
+A step is the whole path over one batch: kv_store of the batch's new rows,
+split-KV paged attention, log-sum-exp merge.  The default workload is the
+Llama-3-8B-shaped decode batch (B=32, 32 q / 8 kv heads, D=128, bf16,
+page_size 16, seq_len 4096, 9000-page pool, shuffled page table).
+
+Timing: W untimed steps, then exactly K steps between two device
+synchronisations.  Consecutive steps read different copies of the pool
+("layers"), so no step finds the previous step's K/V in the 256 MB Infinity
+Cache.  Per-kernel durations come from HIP events recorded on the stream the
+kernels run on.  Prints ONE JSON line on stdout; details go to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--layers", type=int, default=3, help="pool copies rotated over consecutive steps")
+    ap.add_argument("--splits", type=int, default=None, help="override the split heuristic")
+    ap.add_argument("--store-reps", type=int, default=20, help="timed bulk-fill kv_store launches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the step would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_gqa_store_amd as pkv
+    from paged_kv_gqa_store_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.config]
+    log(f"[bench] workload {cfg.name}: {cfg.describe()}")
+    t = time.perf_counter()
+    inp = W.make_inputs(cfg)
+    log(f"[bench] inputs drawn in {time.perf_counter() - t:.1f} s")
+
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    q = to_bf16(inp.q)
+    k_new, v_new = to_bf16(inp.k_new), to_bf16(inp.v_new)
+    page_table, seq_lens, slots = to_i32(inp.page_table), to_i32(inp.seq_lens), to_i32(inp.slot_mapping)
+    k0, v0 = to_bf16(inp.k_pool), to_bf16(inp.v_pool)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.layers - 1)]
+    B, Hq, Hkv, D, P = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.P
+    max_len = inp.max_seq_len
+    S = args.splits or pkv.num_splits(B, Hkv, max_len, P)
+    o_p, l_p = pkv.workspace(B, Hq, D, S, dev)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    log(f"[bench] num_splits {S}, chunk {pkv.split_chunk(max_len, S, P)}, layers {args.layers}")
+
+    def step(i, ev=None):
+        kp, vp = pools[i % len(pools)]
+        if ev is not None:
+            ev[0].record()
+        pkv.kv_store(kp, vp, k_new, v_new, slots)
+        if ev is not None:
+            ev[1].record()
+        pkv.paged_decode_attn(q, kp, vp, page_table, seq_lens, max_len, S, o_partial=o_p, lse_partial=l_p)
+        if ev is not None:
+            ev[2].record()
+        pkv.decode_merge(o_p, l_p, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    store_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    merge_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+
+    kv_b = W.kv_bytes(inp.seq_lens, Hkv, D)
+    terms = W.attention_bytes(inp.seq_lens, Hq, Hkv, D, P, S)
+    # bytes the attention kernel itself must move: K+V, q, page ids, partials written once
+    attn_kernel_b = terms["kv"] + terms["q"] + terms["page_ids"] + terms["partials"] // 2
+    attn_us = float(attn_ms.mean() * 1e3)
+    achieved = attn_kernel_b / (attn_us * 1e-6) / 1e9
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us (wall) | store {store_ms.mean() * 1e3:.1f} us | "
+        f"attn {attn_us:.1f} us (median {np.median(attn_ms) * 1e3:.1f}) | merge {merge_ms.mean() * 1e3:.1f} us")
+    log(f"[bench] attention kernel {achieved:.0f} GB/s = {achieved / PEAK_HBM_GBPS:.1%} of {PEAK_HBM_GBPS:.0f} GB/s")
+
+    # kv_store bandwidth: bulk fill of every position (prefill-style), same kernel and ABI
+    k_rows, v_rows, bslots = W.bulk_fill_rows(inp)
+    k_rows_d, v_rows_d, bslots_d = to_bf16(k_rows), to_bf16(v_rows), to_i32(bslots)
+    row_b = cfg.row_elems * 2
+    store_b = W.store_bytes(bslots.shape[0], row_b)
+    for i in range(3):
+        kp, vp = pools[i % len(pools)]
+        pkv.kv_store(kp, vp, k_rows_d, v_rows_d, bslots_d)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.store_reps)]
+    torch.cuda.synchronize()
+    for i in range(args.store_reps):
+        kp, vp = pools[i % len(pools)]
+        sev[i][0].record()
+        pkv.kv_store(kp, vp, k_rows_d, v_rows_d, bslots_d)
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    bulk_us = float(np.mean([a.elapsed_time(b) for a, b in sev]) * 1e3)
+    store_gbps = store_b / (bulk_us * 1e-6) / 1e9
+    log(f"[bench] kv_store bulk fill: {bslots.shape[0]} rows, {store_b / 1e6:.1f} MB in {bulk_us:.1f} us = "
+        f"{store_gbps:.0f} GB/s ({store_gbps / PEAK_HBM_GBPS:.1%})")
+    del k_rows_d, v_rows_d, bslots_d
+
+    result = {
+        "metric": "paged decode attn µs/step + achieved HBM GB/s (% of peak); kv_store GB/s",
+        "value": round(kv_b / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name} (decode step: kv_store + split-KV paged attention + merge)",
+            "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
+            "seq_len": cfg.seq_len if cfg.seq_len else "ragged", "pool_pages": cfg.num_pages,
+            "num_splits": S, "layers_rotated": len(pools),
+        },
+        "value_definition": "K+V bytes read per step / wall time of the whole step (store + attention + merge)",
+        "attn_us_per_step": round(attn_us + float(merge_ms.mean() * 1e3), 2),
+        "attn_kernel_us": round(attn_us, 2),
+        "merge_kernel_us": round(float(merge_ms.mean() * 1e3), 2),
+        "store_step_us": round(float(store_ms.mean() * 1e3), 2),
+        "attn_kv_GBps": round(kv_b / ((attn_us + merge_ms.mean() * 1e3) * 1e-6) / 1e9, 1),
+        "attn_pct_of_peak": round(100 * kv_b / ((attn_us + merge_ms.mean() * 1e3) * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+        "kv_store_bulk_GBps": round(store_gbps, 1),
+        "kv_store_bulk_pct_of_peak": round(100 * store_gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode (split-KV attention)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": attn_kernel_b,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        kf, vf = inp.pools_after_store()
+        flat = lambda a: a.reshape(cfg.num_pages * P, cfg.row_elems)
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and reps < 1000:
+            t = time.perf_counter()
+            oracle.kv_store(flat(inp.k_pool), flat(inp.v_pool), inp.k_new, inp.v_new, inp.slot_mapping)
+            oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+            t_cpu += time.perf_counter() - t
+            reps += 1
+        cpu_gbps = kv_b * reps / t_cpu / 1e9
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbps, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the full {cfg.name} step (oracle store + fp64 attention), {reps} run(s), "
+                      f"{t_cpu:.1f} s on {cpu_model()}",
+            "ms_per_step": round(t_cpu / reps * 1e3, 2),
+        }
+        log(f"[bench] oracle: {t_cpu / reps * 1e3:.1f} ms/step on {oracle.num_threads()} threads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: one decode step of grouped-query attention
+ * over a paged KV cache, on AMD MI355X (gfx950).
+ *
+ *   pkv_kv_store          scatter the step's new K/V rows into the page pool
+ *   pkv_paged_decode_attn split-KV attention through the page table -> partials
+ *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
+ *   pkv_num_splits        split-count heuristic (host only)
+ *   pkv_split_chunk       positions per split for a split count (host only)
+ *   pkv_status_str        text of a status code
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless stated; every buffer belongs to the
+ *     caller.  The library never allocates, frees or synchronises: each call
+ *     validates its arguments on the host, enqueues its kernels on `stream`
+ *     (a hipStream_t; NULL = the default stream) and returns.
+ *   - A negative status means that nothing was launched (except PKV_ERR_HIP,
+ *     reported when the launch itself failed).
+ *   - Device-side preconditions are not checked on the host (that would need a
+ *     synchronisation); the kernels never access memory outside the buffers
+ *     the sizes describe, whatever the index contents (see each call).
+ *
+ * Layouts (bf16 = 2-byte IEEE bfloat16 bit patterns, row-major):
+ *   q            [B, Hq, D]                      contiguous
+ *   k_pool/v_pool[num_pages, page_size, Hkv, D]  == [num_slots, Hkv*D] rows
+ *   page_table   int32 [B, max_pages_per_seq]    page ids of each sequence, in order
+ *   seq_lens     int32 [B]                       tokens of each sequence, the new one included
+ *   slot_mapping int32 [n]                       destination slot of each new row
+ *   o_partial    fp32 [B, Hq, num_splits, D]     normalised per-split outputs
+ *   lse_partial  fp32 [B, Hq, num_splits]        per-split natural-log sum-exp
+ *   out          bf16 [B, Hq, D];  lse_out fp32 [B, Hq] (optional)
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+
+#define PKV_OK 0
+#define PKV_ERR_NULL (-1)        /* a required pointer is NULL                       */
+#define PKV_ERR_SHAPE (-2)       /* a size is out of range or inconsistent           */
+#define PKV_ERR_UNSUPPORTED (-3) /* head_dim / group size / page size not supported  */
+#define PKV_ERR_ALIGN (-4)       /* a base pointer or stride is not 16-byte aligned  */
+#define PKV_ERR_HIP (-5)         /* the HIP runtime reported a launch failure        */
+
+/*
+ * pkv_kv_store -- write n new rows into the K and V pools by slot index.
+ *
+ * Follows: mini-sglang handbook, "Custom CUDA kernels", section "Moving whole
+ * rows by index" (k_cache[out_loc[i]] <- k[i], same for v; a pure row move)
+ * and section "Hooking into PyTorch" (int32 indices, rows contiguous, free row
+ * strides, n == 0 returns at once, the stream handed in by the caller).
+ *
+ *   k_pool, v_pool    device, num_slots rows of pool_row_stride elements
+ *   k_new, v_new      device, n rows of in_row_stride elements
+ *   slot_mapping      device int32 [n]; row i goes to slot slot_mapping[i]
+ *   row_elems         elements copied per row (Hkv*D); <= both strides
+ *   elem_bytes        1, 2, 4 or 8 (2 for bf16)
+ * Strides are in elements.  Rows move in 16-byte units when both bases, both
+ * strides and the row length are 16-byte multiples, otherwise in the largest
+ * unit (8, 4, 2, 1 bytes) that divides all of them; the bytes written are
+ * identical either way.
+ * Preconditions (device): slots distinct.  A slot outside [0, num_slots) is
+ * skipped, never written.  Two rows naming one slot race.
+ * Returns PKV_OK (n == 0: nothing launched), PKV_ERR_NULL, PKV_ERR_SHAPE,
+ * PKV_ERR_UNSUPPORTED (elem_bytes), PKV_ERR_HIP.
+ */
+pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_row_stride,
+                        const void *k_new, const void *v_new, int64_t in_row_stride,
+                        const int32_t *slot_mapping, int64_t n, int64_t row_elems,
+                        int32_t elem_bytes, void *stream);
+
+/*
+ * pkv_paged_decode_attn -- split-KV decode attention over the paged pool.
+ *
+ * Follows: AstrAI "CUDA Kernels", section "Overview" (split-KV GQA decode, the
+ * paged source shares the kernel body), section "Q Scheduling and KV
+ * Addressing" (the paged source turns a logical position into a physical
+ * address; the q heads of one kv-head group share each K/V tile), section
+ * "Python Wrappers" (scale 1/sqrt(head_dim)).
+ *
+ * For every sequence b, q head h (kv head g = h / (Hq/Hkv)) and split s, over
+ * positions t in [s*chunk, min((s+1)*chunk, seq_lens[b])) with
+ * chunk = pkv_split_chunk(max_seq_len, num_splits, page_size) and slot
+ * r(t) = page_table[b, t / page_size] * page_size + t % page_size:
+ *     x_t = scale * <q[b,h,:], K[r(t), g, :]>
+ *     o_partial[b,h,s,:]  = sum_t softmax(x)_t V[r(t), g, :]
+ *     lse_partial[b,h,s]  = ln sum_t exp(x_t)
+ * fp32 arithmetic on the bf16 inputs.  An empty range writes o = 0 and
+ * lse = -inf.  Every element of o_partial / lse_partial is written.
+ *
+ *   head_dim D in {64, 128}; group Hq/Hkv in {1, 2, 4, 8}; page_size a power of
+ *   two in [1, 1024]; num_splits in [1, 1024]; max_seq_len in [0, max_pages_per_seq*page_size].
+ *   q, k_pool, v_pool 16-byte aligned (else PKV_ERR_ALIGN).
+ * Preconditions (device): seq_lens[b] <= max_seq_len.  Positions past
+ * num_splits*chunk are not visited.  A page id outside [0, num_pages) makes
+ * that row's output NaN instead of being read.
+ */
+pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *page_table, const int32_t *seq_lens, int32_t B,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                 int32_t num_pages, int32_t max_pages_per_seq,
+                                 int32_t max_seq_len, int32_t num_splits, float scale,
+                                 float *o_partial, float *lse_partial, void *stream);
+
+/*
+ * pkv_decode_merge -- combine the split partials of every (b, h) row.
+ *
+ * Follows: cuDNN frontend "CSA Fused Compressor", section "ratio=128" (chunked
+ * softmax: per-chunk (max, denominator, accumulator) triples merged in one
+ * fixed order) and section "Numerics" (fp32 throughout, one final bf16
+ * rounding, bitwise run-to-run determinism).
+ *     M = max_s lse_s,  w_s = exp(lse_s - M)
+ *     out = bf16_rne( sum_s w_s o_s / sum_s w_s )   (s ascending)
+ *     lse_out = M + ln sum_s w_s                    (if lse_out != NULL)
+ * A row whose splits are all empty gives out = 0 and lse_out = -inf.
+ *   D in {64, 128}; num_splits in [1, 1024]; out 16-byte aligned.
+ */
+pkv_status pkv_decode_merge(const float *o_partial, const float *lse_partial, int32_t B,
+                            int32_t Hq, int32_t D, int32_t num_splits, void *out, float *lse_out,
+                            void *stream);
+
+/*
+ * pkv_num_splits -- split count for a batch (host only, no GPU call).
+ *
+ * The pages only say the launcher does the split-K arithmetic and that small
+ * batches underfill the GPU despite split-KV (AstrAI "CUDA Kernels", sections
+ * "File Layout" and "Known Optimization Targets"); the rule is a reading:
+ *     S_fill = ceil(2*num_cus / (B*Hkv))     enough workgroups to fill the GPU
+ *     S_bal  = ceil(max_seq_len / 2048)      splits of at most 2048 positions
+ *     S      = clamp(max(S_fill, S_bal), 1, max(1, ceil(max_seq_len / 256)))
+ * Returns >= 1 for valid arguments, PKV_ERR_SHAPE otherwise.
+ */
+int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
+                       int32_t num_cus);
+
+/* pkv_split_chunk -- positions covered by one split: the smallest multiple of
+ * page_size >= ceil(max_seq_len / num_splits).  0 if max_seq_len == 0,
+ * PKV_ERR_SHAPE for invalid arguments.  Host only. */
+int32_t pkv_split_chunk(int32_t max_seq_len, int32_t num_splits, int32_t page_size);
+
+/* pkv_status_str -- static text for a status code (never NULL). */
+const char *pkv_status_str(pkv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

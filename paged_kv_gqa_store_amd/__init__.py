@@ -1,0 +1,17 @@
+"""Paged-KV grouped-query attention decode step for AMD MI355X (gfx950).
+
+One decode step is three hand-written HIP kernels behind a C ABI
+(``include/pkv.h``, ``libpkv.so``):
+
+* ``kv_store``           scatter the step's new K/V rows into the page pool;
+* ``paged_decode_attn``  split-KV attention over pages found through a page table;
+* ``decode_merge``       log-sum-exp merge of the split partials.
+
+The binding in :mod:`paged_kv_gqa_store_amd.ops` only marshals arguments;
+PyTorch provides device memory and streams.  Loading the library is lazy, and
+every op raises ``RuntimeError`` if ``libpkv.so`` is missing: there is no
+fallback implementation.
+"""
+from .ops import (  # noqa: F401
+    decode_merge, decode_step, kv_store, num_splits, paged_decode_attn, split_chunk, workspace,
+)

@@ -1,0 +1,158 @@
+// The exported C ABI of libpkv.so (declared in include/pkv.h): argument
+// validation on the host, then one launch per kernel on the caller's stream.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "pkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2_exact(int64_t x) {
+  int k = 0;
+  while ((int64_t(1) << k) < x) ++k;
+  return k;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Largest copy unit (16, 8, 4, 2 or 1 bytes) dividing every address and length.
+int copy_unit(std::initializer_list<uint64_t> vals) {
+  for (int u = 16; u > 1; u >>= 1) {
+    bool ok = true;
+    for (uint64_t v : vals) ok = ok && (v % uint64_t(u) == 0);
+    if (ok) return u;
+  }
+  return 1;
+}
+
+constexpr int kMaxSplits = 1024;
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_str(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "pkv: a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "pkv: a size is out of range or inconsistent";
+    case PKV_ERR_UNSUPPORTED: return "pkv: head_dim, group size or page size not supported";
+    case PKV_ERR_ALIGN: return "pkv: a base pointer or stride is not 16-byte aligned";
+    case PKV_ERR_HIP: return "pkv: HIP launch failed";
+    default: return "pkv: unknown status";
+  }
+}
+
+int32_t pkv_split_chunk(int32_t max_seq_len, int32_t num_splits, int32_t page_size) {
+  if (max_seq_len < 0 || num_splits < 1 || !is_pow2(page_size)) return PKV_ERR_SHAPE;
+  if (max_seq_len == 0) return 0;
+  const int64_t per = ceil_div(max_seq_len, num_splits);
+  return int32_t(ceil_div(per, page_size) * page_size);
+}
+
+int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
+                       int32_t num_cus) {
+  if (B < 1 || Hkv < 1 || max_seq_len < 0 || !is_pow2(page_size) || num_cus < 1)
+    return PKV_ERR_SHAPE;
+  const int64_t groups = int64_t(B) * Hkv;
+  const int64_t s_fill = ceil_div(2 * int64_t(num_cus), groups);
+  const int64_t s_bal = ceil_div(max_seq_len, 2048);
+  int64_t s = s_fill > s_bal ? s_fill : s_bal;
+  int64_t cap = ceil_div(max_seq_len, 256);
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return int32_t(s < 1 ? 1 : s);
+}
+
+pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_row_stride,
+                        const void *k_new, const void *v_new, int64_t in_row_stride,
+                        const int32_t *slot_mapping, int64_t n, int64_t row_elems,
+                        int32_t elem_bytes, void *stream) {
+  if (n < 0 || num_slots < 0 || row_elems < 0) return PKV_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return PKV_ERR_UNSUPPORTED;
+  if (n == 0 || row_elems == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
+  if (row_elems > pool_row_stride || row_elems > in_row_stride) return PKV_ERR_SHAPE;
+  const int64_t row_b = row_elems * elem_bytes;
+  const int64_t pool_stride_b = pool_row_stride * elem_bytes;
+  const int64_t in_stride_b = in_row_stride * elem_bytes;
+  if (num_slots > (int64_t(1) << 31) || n > (int64_t(1) << 40)) return PKV_ERR_SHAPE;
+  const int unit = copy_unit({uint64_t(row_b), uint64_t(pool_stride_b), uint64_t(in_stride_b),
+                              reinterpret_cast<uintptr_t>(k_pool), reinterpret_cast<uintptr_t>(v_pool),
+                              reinterpret_cast<uintptr_t>(k_new), reinterpret_cast<uintptr_t>(v_new)});
+  hipError_t e = pkv::launch_kv_store(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new,
+                                      in_stride_b, slot_mapping, n, row_b, unit,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *page_table, const int32_t *seq_lens, int32_t B,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                 int32_t num_pages, int32_t max_pages_per_seq,
+                                 int32_t max_seq_len, int32_t num_splits, float scale,
+                                 float *o_partial, float *lse_partial, void *stream) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_seq_len < 0 ||
+      num_splits < 1 || num_splits > kMaxSplits)
+    return PKV_ERR_SHAPE;
+  if (Hq % Hkv) return PKV_ERR_SHAPE;
+  const int G = Hq / Hkv;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size > 1024) return PKV_ERR_UNSUPPORTED;
+  if (int64_t(max_seq_len) > int64_t(max_pages_per_seq) * page_size) return PKV_ERR_SHAPE;
+  if (B > 65535 || Hkv > 65535) return PKV_ERR_SHAPE;
+  if (int64_t(num_pages) * page_size > (int64_t(1) << 31)) return PKV_ERR_SHAPE;
+  if (int64_t(max_pages_per_seq) * page_size > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return PKV_ERR_SHAPE;
+  if (B == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o_partial || !lse_partial)
+    return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_ALIGN;
+
+  pkv::DecodeParams p;
+  p.q = static_cast<const uint16_t *>(q);
+  p.k_pool = static_cast<const uint16_t *>(k_pool);
+  p.v_pool = static_cast<const uint16_t *>(v_pool);
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.o_partial = o_partial;
+  p.lse_partial = lse_partial;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.G = G;
+  p.page_log2 = log2_exact(page_size);
+  p.num_pages = num_pages;
+  p.max_pages = max_pages_per_seq;
+  p.num_splits = num_splits;
+  p.chunk = max_seq_len == 0 ? page_size : pkv_split_chunk(max_seq_len, num_splits, page_size);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_decode_merge(const float *o_partial, const float *lse_partial, int32_t B,
+                            int32_t Hq, int32_t D, int32_t num_splits, void *out, float *lse_out,
+                            void *stream) {
+  if (B < 0 || Hq < 1 || num_splits < 1 || num_splits > kMaxSplits) return PKV_ERR_SHAPE;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (int64_t(B) * Hq > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
+  if (B == 0) return PKV_OK;
+  if (!o_partial || !lse_partial || !out) return PKV_ERR_NULL;
+  if (!aligned16(out) || !aligned16(o_partial)) return PKV_ERR_ALIGN;
+  hipError_t e = pkv::launch_decode_merge(o_partial, lse_partial, B * Hq, D, num_splits,
+                                          static_cast<uint16_t *>(out), lse_out,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Host-side launchers of the libpkv kernels (internal header; the exported
+// C ABI lives in include/pkv.h and validates every argument before these run).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Arguments of one split-KV decode launch, already validated.
+struct DecodeParams {
+  const uint16_t *q;         // [B, Hq, D] bf16
+  const uint16_t *k_pool;    // [num_pages, P, Hkv, D] bf16
+  const uint16_t *v_pool;
+  const int32_t *page_table; // [B, max_pages]
+  const int32_t *seq_lens;   // [B]
+  float *o_partial;          // [B, Hq, S, D]
+  float *lse_partial;        // [B, Hq, S]
+  int B, Hq, Hkv, D, G;
+  int page_log2;             // page_size = 1 << page_log2
+  int num_pages, max_pages;
+  int num_splits, chunk;     // split s covers [s*chunk, (s+1)*chunk)
+  float scale_log2;          // softmax scale * log2(e)
+};
+
+hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,
+                           const void *k_new, const void *v_new, int64_t in_stride_b,
+                           const int32_t *slots, int64_t n, int64_t row_b, int unit_b,
+                           hipStream_t stream);
+
+hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
+
+hipError_t launch_decode_merge(const float *o_partial, const float *lse_partial, int rows, int D,
+                               int num_splits, uint16_t *out, float *lse_out, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,101 @@
+// kv_store: scatter the step's new K/V rows into the page pool by slot index.
+//
+// Follows the mini-sglang handbook, "Custom CUDA kernels", section "Moving
+// whole rows by index": a pure row move, bound by memory bandwidth, copied in
+// 16-byte vectors when the row and its strides allow it.  The gfx950 design:
+//   - wave64; a row gets 2^k lanes (k chosen on the host so a 2 KB row is one
+//     wave and a 128 B row is 8 lanes: several short rows share a wave);
+//   - every lane issues all of its loads (K and V) before its first store, so
+//     each wave keeps 2 * units_per_lane 16-byte loads in flight;
+//   - a slot outside the pool is skipped, so a bad index cannot fault.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+// Copies rows with UNITS (compile-time) copy units per lane, unit type U.
+// Row r of the inputs goes to pool row slots[r]; lanes_log2 lanes per row.
+template <typename U, int UNITS>
+__global__ __launch_bounds__(256) void store_rows_kernel(
+    U *__restrict__ k_pool, U *__restrict__ v_pool, int64_t num_slots, int64_t pool_stride,
+    const U *__restrict__ k_new, const U *__restrict__ v_new, int64_t in_stride,
+    const int32_t *__restrict__ slots, int64_t n, int64_t row_units, int lanes_log2) {
+  const int64_t lanes = int64_t(1) << lanes_log2;
+  const int64_t rows_per_grid = (int64_t(gridDim.x) * blockDim.x) >> lanes_log2;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t lane = gid & (lanes - 1);
+  for (int64_t r = gid >> lanes_log2; r < n; r += rows_per_grid) {
+    const int64_t slot = slots[r];
+    if (slot < 0 || slot >= num_slots) continue;
+    const U *ks = k_new + r * in_stride;
+    const U *vs = v_new + r * in_stride;
+    U *kd = k_pool + slot * pool_stride;
+    U *vd = v_pool + slot * pool_stride;
+    for (int64_t base = 0; base < row_units; base += UNITS * lanes) {
+      U kb[UNITS], vb[UNITS];
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u) {
+        const int64_t i = base + u * lanes + lane;
+        if (i < row_units) {
+          kb[u] = ks[i];
+          vb[u] = vs[i];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u) {
+        const int64_t i = base + u * lanes + lane;
+        if (i < row_units) {
+          kd[i] = kb[u];
+          vd[i] = vb[u];
+        }
+      }
+    }
+  }
+}
+
+template <typename U>
+hipError_t launch_unit(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,
+                       const void *k_new, const void *v_new, int64_t in_stride_b,
+                       const int32_t *slots, int64_t n, int64_t row_b, hipStream_t stream) {
+  const int64_t row_units = row_b / int64_t(sizeof(U));
+  // lanes per row: the power of two covering the row, at most one wave
+  int lanes_log2 = 0;
+  while ((int64_t(1) << lanes_log2) < row_units && lanes_log2 < 6) ++lanes_log2;
+  const int64_t lanes = int64_t(1) << lanes_log2;
+  const int64_t units_per_lane = (row_units + lanes - 1) / lanes;
+  const int64_t rows_per_block = 256 / lanes;
+  int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
+  // enough blocks to fill 256 CUs many times over; the grid-stride loop does the rest
+  if (blocks > 65536) blocks = 65536;
+  const dim3 grid{unsigned(blocks)}, block{256};
+  U *kp = static_cast<U *>(k_pool);
+  U *vp = static_cast<U *>(v_pool);
+  const U *kn = static_cast<const U *>(k_new);
+  const U *vn = static_cast<const U *>(v_new);
+  const int64_t ps = pool_stride_b / int64_t(sizeof(U)), is = in_stride_b / int64_t(sizeof(U));
+  if (units_per_lane >= 2)
+    hipLaunchKernelGGL((store_rows_kernel<U, 2>), grid, block, 0, stream, kp, vp, num_slots, ps,
+                       kn, vn, is, slots, n, row_units, lanes_log2);
+  else
+    hipLaunchKernelGGL((store_rows_kernel<U, 1>), grid, block, 0, stream, kp, vp, num_slots, ps,
+                       kn, vn, is, slots, n, row_units, lanes_log2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,
+                           const void *k_new, const void *v_new, int64_t in_stride_b,
+                           const int32_t *slots, int64_t n, int64_t row_b, int unit_b,
+                           hipStream_t stream) {
+  switch (unit_b) {
+    case 16: return launch_unit<uint4>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
+    case 8: return launch_unit<uint2>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
+    case 4: return launch_unit<uint32_t>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
+    case 2: return launch_unit<uint16_t>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
+    default: return launch_unit<uint8_t>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,168 @@
+"""Python binding of libpkv: argument marshalling only.
+
+Every function checks dtypes, devices and contiguity, passes raw device
+pointers and the current HIP stream to the C ABI (``include/pkv.h``) and raises
+``RuntimeError`` on a nonzero status.  All arithmetic of the decode step runs
+in the library's HIP kernels; PyTorch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._lib import check, lib
+
+_num_cus_cache: dict = {}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise RuntimeError(msg)
+
+
+def _on_gpu(*ts):
+    dev = ts[0].device
+    for t in ts:
+        _require(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+
+
+def num_cus(device=None) -> int:
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    key = device.index
+    if key not in _num_cus_cache:
+        _num_cus_cache[key] = torch.cuda.get_device_properties(device).multi_processor_count
+    return _num_cus_cache[key]
+
+
+def num_splits(B: int, Hkv: int, max_seq_len: int, page_size: int, n_cus: int | None = None) -> int:
+    """The split-count heuristic of the library (host only)."""
+    n_cus = num_cus() if n_cus is None else n_cus
+    s = lib().pkv_num_splits(B, Hkv, max_seq_len, page_size, n_cus)
+    check(min(s, 0), "pkv_num_splits")
+    return s
+
+
+def split_chunk(max_seq_len: int, num_splits: int, page_size: int) -> int:
+    c = lib().pkv_split_chunk(max_seq_len, num_splits, page_size)
+    check(min(c, 0), "pkv_split_chunk")
+    return c
+
+
+def _rows(t: torch.Tensor, name: str, pool: bool) -> torch.Tensor:
+    """View a pool ([num_slots,row] or [num_pages,P,Hkv,D]) or a batch of new rows
+    ([n,row] or [n,Hkv,D]) as 2-D rows, never copying (a copy would hide the writes)."""
+    if t.dim() == 2:
+        v = t
+    elif pool and t.dim() == 4:
+        v = t.view(t.shape[0] * t.shape[1], t.shape[2] * t.shape[3])
+    elif not pool and t.dim() == 3:
+        v = t.view(t.shape[0], t.shape[1] * t.shape[2])
+    else:
+        raise RuntimeError(f"{name}: unsupported rank {t.dim()}")
+    _require(v.stride(1) == 1, f"{name}: rows must be contiguous")
+    return v
+
+
+def kv_store(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             slot_mapping: torch.Tensor) -> None:
+    """Scatter ``k_new[i]`` / ``v_new[i]`` into pool row ``slot_mapping[i]`` (in place).
+
+    Pools: ``[num_slots, row]`` or ``[num_pages, page_size, Hkv, D]``; new rows:
+    ``[n, row]`` or ``[n, Hkv, D]``.  Row strides may be anything; elements of
+    a row must be contiguous."""
+    _on_gpu(k_pool, v_pool, k_new, v_new, slot_mapping)
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1 and slot_mapping.is_contiguous(),
+             "slot_mapping must be a contiguous int32 vector")
+    kp, vp = _rows(k_pool, "k_pool", True), _rows(v_pool, "v_pool", True)
+    kn, vn = _rows(k_new, "k_new", False), _rows(v_new, "v_new", False)
+    _require(kp.shape == vp.shape and kp.stride() == vp.stride(), "k_pool and v_pool must match")
+    _require(kn.shape == vn.shape and kn.stride() == vn.stride(), "k_new and v_new must match")
+    _require(kp.dtype == vp.dtype == kn.dtype == vn.dtype, "pool and rows must share a dtype")
+    n = slot_mapping.shape[0]
+    _require(kn.shape[0] == n, "one slot per new row")
+    _require(kn.shape[1] == kp.shape[1], "new rows and pool rows must have the same length")
+    st = lib().pkv_kv_store(kp.data_ptr(), vp.data_ptr(), kp.shape[0], kp.stride(0),
+                            kn.data_ptr(), vn.data_ptr(), kn.stride(0), slot_mapping.data_ptr(), n,
+                            kn.shape[1], kn.element_size(), _stream(kp))
+    check(st, "pkv_kv_store")
+
+
+def workspace(B: int, Hq: int, D: int, splits: int, device) -> tuple[torch.Tensor, torch.Tensor]:
+    """Partial buffers for :func:`paged_decode_attn`: o ``[B,Hq,S,D]`` fp32, lse ``[B,Hq,S]`` fp32."""
+    return (torch.empty((B, Hq, splits, D), dtype=torch.float32, device=device),
+            torch.empty((B, Hq, splits), dtype=torch.float32, device=device))
+
+
+def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
+                      splits: int | None = None, scale: float | None = None,
+                      o_partial=None, lse_partial=None):
+    """Split-KV attention over the paged pool; returns (o_partial, lse_partial).
+
+    q ``[B,Hq,D]`` bf16; pools ``[num_pages,P,Hkv,D]`` bf16; page_table int32
+    ``[B,max_pages]``; seq_lens int32 ``[B]``; ``max_seq_len`` is a host bound
+    on ``seq_lens`` (no device read)."""
+    _on_gpu(q, k_pool, v_pool, page_table, seq_lens)
+    _require(q.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
+             "q and the pools must be bfloat16")
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B,Hq,D]")
+    _require(k_pool.dim() == 4 and k_pool.is_contiguous() and v_pool.is_contiguous()
+             and v_pool.shape == k_pool.shape, "pools must be contiguous [num_pages,P,Hkv,D]")
+    _require(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous(),
+             "page_table must be contiguous int32 [B,max_pages]")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens must be int32")
+    B, Hq, D = q.shape
+    num_pages, P, Hkv, D2 = k_pool.shape
+    _require(D2 == D and page_table.shape[0] == B and seq_lens.shape == (B,), "inconsistent shapes")
+    S = num_splits(B, Hkv, max_seq_len, P) if splits is None else splits
+    if o_partial is None or lse_partial is None:
+        o_partial, lse_partial = workspace(B, Hq, D, S, q.device)
+    _require(o_partial.shape == (B, Hq, S, D) and o_partial.dtype == torch.float32 and o_partial.is_contiguous(),
+             "o_partial must be contiguous fp32 [B,Hq,S,D]")
+    _require(lse_partial.shape == (B, Hq, S) and lse_partial.dtype == torch.float32 and lse_partial.is_contiguous(),
+             "lse_partial must be contiguous fp32 [B,Hq,S]")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    st = lib().pkv_paged_decode_attn(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                     page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, P,
+                                     num_pages, page_table.shape[1], max_seq_len, S, scale,
+                                     o_partial.data_ptr(), lse_partial.data_ptr(), _stream(q))
+    check(st, "pkv_paged_decode_attn")
+    return o_partial, lse_partial
+
+
+def decode_merge(o_partial, lse_partial, out=None, lse_out=None, want_lse: bool = False):
+    """Log-sum-exp merge of the split partials -> bf16 ``[B,Hq,D]`` (and fp32 lse ``[B,Hq]``)."""
+    _on_gpu(o_partial, lse_partial)
+    _require(o_partial.dtype == torch.float32 and lse_partial.dtype == torch.float32
+             and o_partial.is_contiguous() and lse_partial.is_contiguous(), "partials must be contiguous fp32")
+    B, Hq, S, D = o_partial.shape
+    _require(lse_partial.shape == (B, Hq, S), "lse_partial must be [B,Hq,S]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=o_partial.device)
+    _require(out.shape == (B, Hq, D) and out.dtype == torch.bfloat16 and out.is_contiguous(),
+             "out must be contiguous bf16 [B,Hq,D]")
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=o_partial.device)
+    if lse_out is not None:
+        _require(lse_out.shape == (B, Hq) and lse_out.dtype == torch.float32 and lse_out.is_contiguous(),
+                 "lse_out must be contiguous fp32 [B,Hq]")
+    st = lib().pkv_decode_merge(o_partial.data_ptr(), lse_partial.data_ptr(), B, Hq, D, S,
+                                out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None,
+                                _stream(o_partial))
+    check(st, "pkv_decode_merge")
+    return (out, lse_out) if (want_lse or lse_out is not None) else out
+
+
+def decode_step(q, k_new, v_new, k_pool, v_pool, page_table, seq_lens, slot_mapping,
+                max_seq_len: int, splits: int | None = None, out=None, ws=None,
+                want_lse: bool = False):
+    """One decode step: store the new rows, split-KV attention, merge."""
+    kv_store(k_pool, v_pool, k_new, v_new, slot_mapping)
+    o_p, l_p = paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits,
+                                 o_partial=None if ws is None else ws[0],
+                                 lse_partial=None if ws is None else ws[1])
+    return decode_merge(o_p, l_p, out=out, want_lse=want_lse)

@@ -17,11 +17,17 @@ granular), with every value synthetic:
 * the step's new token sits at position ``L_b - 1`` (the sequence length
   counts it), its pool slot holds a NaN canary until ``kv_store`` writes it.
 
-Random streams: ``numpy.random.Generator(PCG64(20260000 + config_id))``,
-drawn in the order seq_lens (ragged config only), page permutation, q, K, V.
+Random streams, for seed = 20260000 + config_id:
+``numpy.random.Generator(PCG64(seed))`` draws the lengths (ragged config only)
+and then the page permutation; q, K and V come from the three children of
+``numpy.random.SeedSequence(seed).spawn(3)``, each cut into chunks of 2^22
+values with one PCG64 stream per chunk (so the result does not depend on the
+number of threads that fill it).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -126,16 +132,31 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _normal_bf16(rng, shape, std=1.0, chunk=1 << 24):
-    """Draw N(0, std^2) float32 and round to bf16, in chunks to bound memory."""
+_CHUNK = 1 << 22
+
+
+def _normal_bf16(seed_seq, shape, std=1.0):
+    """N(0, std^2) float32 rounded to bf16.  The array is cut into chunks of
+    2^22 values; chunk i is drawn from PCG64(seed_seq.spawn(...)[i]), so the
+    result does not depend on how many threads fill it."""
     n = int(np.prod(shape))
     out = np.empty(n, np.uint16)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        x = rng.standard_normal(e - s, dtype=np.float32)
+    nchunks = -(-n // _CHUNK)
+    children = seed_seq.spawn(nchunks)
+
+    def fill(i):
+        s, e = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        x = np.random.Generator(np.random.PCG64(children[i])).standard_normal(e - s, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
         out[s:e] = to_bf16_bits(x)
+
+    if nchunks <= 1:
+        for i in range(nchunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
@@ -151,6 +172,7 @@ def make_inputs(cfg: Config, seed: int | None = None, seq_lens=None) -> Inputs:
     """Draw one decode step's inputs for ``cfg`` (see the module docstring)."""
     seed = SEED_BASE + cfg.cid if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
+    q_ss, k_ss, v_ss = np.random.SeedSequence(seed).spawn(3)
     lens = draw_seq_lens(cfg, rng) if seq_lens is None else np.asarray(seq_lens, np.int32)
     B, P = cfg.B, cfg.P
     assert lens.shape == (B,)
@@ -168,12 +190,12 @@ def make_inputs(cfg: Config, seed: int | None = None, seq_lens=None) -> Inputs:
         page_table[b, :n_pages[b]] = perm[starts[b]:starts[b + 1]]
     used = perm[:total]
 
-    q = _normal_bf16(rng, (B, cfg.Hq, cfg.D), cfg.q_std)
+    q = _normal_bf16(q_ss, (B, cfg.Hq, cfg.D), cfg.q_std)
     shape = (cfg.num_pages, P, cfg.Hkv, cfg.D)
     k_full = np.full(shape, BF16_NAN, np.uint16)
     v_full = np.full(shape, BF16_NAN, np.uint16)
-    k_full[used] = _normal_bf16(rng, (total, P, cfg.Hkv, cfg.D))
-    v_full[used] = _normal_bf16(rng, (total, P, cfg.Hkv, cfg.D))
+    k_full[used] = _normal_bf16(k_ss, (total, P, cfg.Hkv, cfg.D))
+    v_full[used] = _normal_bf16(v_ss, (total, P, cfg.Hkv, cfg.D))
     # slots past each sequence's last token are canaries too
     for b in range(B):
         L = int(lens[b])
@@ -221,15 +243,16 @@ def bulk_fill_rows(inp: Inputs, seed: int | None = None):
     (positions in order), the workload on which kv_store bandwidth is measured.
     Returns (k_rows uint16 [n, Hkv*D], v_rows, slots int32 [n])."""
     cfg = inp.cfg
-    rng = np.random.Generator(np.random.PCG64((SEED_BASE + 1000 + cfg.cid) if seed is None else seed))
+    ss = np.random.SeedSequence((SEED_BASE + 1000 + cfg.cid) if seed is None else seed)
+    k_ss, v_ss = ss.spawn(2)
     slots = []
     for b in range(cfg.B):
         t = np.arange(int(inp.seq_lens[b]), dtype=np.int64)
         slots.append(inp.page_table[b, t // cfg.P].astype(np.int64) * cfg.P + t % cfg.P)
     slots = np.concatenate(slots + [np.zeros(0, np.int64)]).astype(np.int32)
     n = slots.shape[0]
-    k_rows = _normal_bf16(rng, (n, cfg.row_elems))
-    v_rows = _normal_bf16(rng, (n, cfg.row_elems))
+    k_rows = _normal_bf16(k_ss, (n, cfg.row_elems))
+    v_rows = _normal_bf16(v_ss, (n, cfg.row_elems))
     return k_rows, v_rows, slots
 
 

@@ -1,0 +1,122 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/pkv.h declares, and its host-only logic and argument validation behave
+(no call here reaches a kernel launch)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from oracle import oracle
+from paged_kv_gqa_store_amd import _lib
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = (ROOT / "include" / "pkv.h").read_text()
+
+OK, NULL, SHAPE, UNSUP, ALIGN = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def declared_symbols():
+    return sorted(set(re.findall(r"^\S.*?\b(pkv_[a-z_0-9]+)\s*\(", HEADER, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(["pkv_kv_store", "pkv_paged_decode_attn", "pkv_decode_merge",
+                                         "pkv_num_splits", "pkv_split_chunk", "pkv_status_str"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert {s[0] for s in _lib.SIGNATURES} == set(declared_symbols())
+
+
+def test_status_strings(lib):
+    for code in [OK, NULL, SHAPE, UNSUP, ALIGN, -5, 7]:
+        assert lib.pkv_status_str(code)
+
+
+def test_split_heuristic_on_the_five_workloads(lib):
+    # B, Hkv, max_seq_len, page_size -> S at 256 CUs
+    cases = {(2, 1, 100, 16): 1, (32, 8, 4096, 16): 2, (64, 8, 8192, 16): 4,
+             (4, 8, 65536, 16): 32, (128, 16, 2048, 1): 1}
+    for args, s in cases.items():
+        assert lib.pkv_num_splits(*args, 256) == s, args
+
+
+def test_split_heuristic_properties(lib):
+    for B in [1, 3, 32, 500]:
+        for Hkv in [1, 8]:
+            for L in [0, 1, 255, 256, 2049, 100000]:
+                s = lib.pkv_num_splits(B, Hkv, L, 16, 256)
+                assert 1 <= s <= max(1, -(-L // 256))
+                if L > 0:
+                    assert s >= -(-L // 2048) or s == max(1, -(-L // 256))
+    assert lib.pkv_num_splits(0, 8, 10, 16, 256) == SHAPE
+    assert lib.pkv_num_splits(1, 8, 10, 12, 256) == SHAPE
+
+
+def test_split_chunk_agrees_with_the_oracle_reading(lib):
+    for L in [1, 15, 16, 17, 100, 4096, 65536, 8191, 123457]:
+        for S in [1, 2, 3, 4, 7, 32, 1024]:
+            for P in [1, 2, 16, 64]:
+                assert lib.pkv_split_chunk(L, S, P) == oracle.split_chunk(L, S, P)
+    assert lib.pkv_split_chunk(0, 4, 16) == 0
+    assert lib.pkv_split_chunk(10, 0, 16) == SHAPE
+
+
+def test_store_validation(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, p, 0, 8, 2, None) == OK           # n == 0: no launch
+    assert lib.pkv_kv_store(None, p, 10, 8, p, p, 8, p, 3, 8, 2, None) == NULL
+    assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, None, 3, 8, 2, None) == NULL
+    assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, p, -1, 8, 2, None) == SHAPE
+    assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, p, 3, 9, 2, None) == SHAPE        # row > stride
+    assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, p, 3, 8, 3, None) == UNSUP
+
+
+def _attn(lib, **kw):
+    p = ctypes.c_void_p(256)
+    a = dict(q=p, k=p, v=p, pt=p, sl=p, B=2, Hq=8, Hkv=2, D=128, P=16, pages=10, mp=4, L=64, S=2,
+             scale=0.088, o=p, lse=p)
+    a.update(kw)
+    return lib.pkv_paged_decode_attn(a["q"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["Hq"], a["Hkv"],
+                                     a["D"], a["P"], a["pages"], a["mp"], a["L"], a["S"], a["scale"],
+                                     a["o"], a["lse"], None)
+
+
+def test_attention_validation(lib):
+    assert _attn(lib, B=0) == OK
+    assert _attn(lib, q=None) == NULL
+    assert _attn(lib, lse=None) == NULL
+    assert _attn(lib, Hq=7) == SHAPE
+    assert _attn(lib, D=96) == UNSUP
+    assert _attn(lib, Hq=32) == UNSUP            # G = 16
+    assert _attn(lib, P=12) == UNSUP
+    assert _attn(lib, L=65) == SHAPE             # beyond max_pages * P
+    assert _attn(lib, S=0) == SHAPE
+    assert _attn(lib, S=1025) == SHAPE
+    assert _attn(lib, scale=0.0) == SHAPE
+    assert _attn(lib, q=ctypes.c_void_p(258)) == ALIGN
+    assert _attn(lib, k=ctypes.c_void_p(264)) == ALIGN
+
+
+def test_merge_validation(lib):
+    p = ctypes.c_void_p(256)
+    assert lib.pkv_decode_merge(p, p, 0, 8, 128, 2, p, None, None) == OK
+    assert lib.pkv_decode_merge(None, p, 2, 8, 128, 2, p, None, None) == NULL
+    assert lib.pkv_decode_merge(p, p, 2, 8, 96, 2, p, None, None) == UNSUP
+    assert lib.pkv_decode_merge(p, p, 2, 8, 128, 0, p, None, None) == SHAPE
+    assert lib.pkv_decode_merge(p, p, 2, 8, 128, 2, ctypes.c_void_p(258), None, None) == ALIGN
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", tmp_path / "missing.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
