@@ -40,9 +40,14 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--layers", type=int, default=3, help="pool copies rotated over consecutive steps")
     ap.add_argument("--splits", type=int, default=None, help="override the split heuristic")
+    ap.add_argument("--kernel", choices=["mfma", "valu"], default="mfma",
+                    help="decode kernel: matrix-core QK^T (default) or all-VALU")
     ap.add_argument("--store-reps", type=int, default=20, help="timed bulk-fill kv_store launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a known-size reference "
+                         "for the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -63,6 +68,7 @@ def main():
               "(see DESIGN.md for how the step would shard). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    os.environ["PKV_DECODE_KERNEL"] = args.kernel
     import torch
 
     import paged_kv_gqa_store_amd as pkv
@@ -171,7 +177,7 @@ def main():
             "workload": f"{cfg.name} (decode step: kv_store + split-KV paged attention + merge)",
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
             "seq_len": cfg.seq_len if cfg.seq_len else "ragged", "pool_pages": cfg.num_pages,
-            "num_splits": S, "layers_rotated": len(pools),
+            "num_splits": S, "layers_rotated": len(pools), "decode_kernel": args.kernel,
         },
         "value_definition": "K+V bytes read per step / wall time of the whole step (store + attention + merge)",
         "attn_us_per_step": round(attn_us + float(merge_ms.mean() * 1e3), 2),
@@ -193,6 +199,15 @@ def main():
             "algorithmic_bytes_per_launch": attn_kernel_b,
         },
     }
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+        del src, dst
 
     if not args.no_cpu_baseline:
         from oracle import oracle

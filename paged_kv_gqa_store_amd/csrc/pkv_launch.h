@@ -28,7 +28,12 @@ hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_
                            const int32_t *slots, int64_t n, int64_t row_b, int unit_b,
                            hipStream_t stream);
 
+// Split-KV decode.  The matrix-core kernel runs by default; PKV_DECODE_KERNEL=valu
+// in the environment selects the all-VALU kernel instead (kept as the measured
+// baseline of that design choice; both honour the same contract).
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_paged_decode_valu(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_paged_decode_mfma(const DecodeParams &p, hipStream_t stream);
 
 hipError_t launch_decode_merge(const float *o_partial, const float *lse_partial, int rows, int D,
                                int num_splits, uint16_t *out, float *lse_out, hipStream_t stream);

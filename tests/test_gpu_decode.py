@@ -18,6 +18,13 @@ pytestmark = pytest.mark.gpu
 _cache = {}
 
 
+@pytest.fixture(autouse=True, params=["mfma", "valu"])
+def decode_kernel(request, monkeypatch):
+    """Every test runs on both decode kernels (matrix-core default and all-VALU)."""
+    monkeypatch.setenv("PKV_DECODE_KERNEL", request.param)
+    return request.param
+
+
 def inputs(cid):
     if cid not in _cache:
         _cache.clear()
