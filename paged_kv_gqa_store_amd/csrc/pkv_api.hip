@@ -136,6 +136,7 @@ pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *
   p.num_splits = num_splits;
   p.chunk = max_seq_len == 0 ? page_size : pkv_split_chunk(max_seq_len, num_splits, page_size);
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.waves = 4;
   hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

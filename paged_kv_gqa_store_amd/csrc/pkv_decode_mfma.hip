@@ -7,17 +7,21 @@
 //
 // What runs where, per 16-token tile and per wave:
 //   QK^T   one v_mfma_f32_16x16x32_bf16 per 32 dims: A = the group's q rows
-//          (heads on M, zero-padded to 16), B = K^T (tokens on N).  Each lane
-//          loads its 8-dim K slice straight from HBM into the B operand: no
-//          conversion and no LDS staging of K.
+//          (heads on M, zero-padded to 16), B = K^T (tokens on N).  K is read
+//          from HBM as whole rows (every load instruction covers 4 or 8 full
+//          rows: instructions that touch 16 rows x 64 B each measured ~25%
+//          slower on gfx950) and re-laid into the B operand through a padded
+//          per-wave LDS tile.
 //   softmax   scores stay in the MFMA output layout (lane = token, register
 //          = head); tile max by DPP row rotations within the 16-lane row;
 //          exp2 on v_exp_f32 (q scale folded with log2 e).
 //   P.V    on the VALU in fp32: a lane owns 8 dims of one token's V row per
 //          load, p is broadcast from the score layout through a small LDS
 //          slot; the accumulator is rescaled only when a head's max moved.
-//   K/V of the next tile are in flight while a tile is computed; page ids
-//   are loaded one tile further ahead.
+//   Page ids of a split are staged in LDS (fetched together with the
+//   sequence length); each wave streams a contiguous range of tiles through
+//   a ring of register buffers, with two (D=128) or three (D=64) tiles in
+//   flight while one is computed.
 #include <math.h>
 
 #include "pkv_device.h"
@@ -26,13 +30,24 @@
 namespace pkv {
 namespace {
 
+// Native vector types only in the hot loop: HIP's uint4/float4 are structs,
+// and a struct copy into LDS becomes a memcpy that pins its source to scratch.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
 constexpr int kTile = 16;  // tokens per tile = N of one 16x16x32 MFMA
+constexpr int kSegPages = 2048;  // page ids held in LDS at a time
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void unpack8v(const u32x4 &v, float f[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(v[i]);
+    f[2 * i + 1] = bf16_hi(v[i]);
+  }
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -59,7 +74,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, int G, bool kPageTile>
+// Keeps the prefetch loads issued before it where they are: a compiler memory
+// barrier (no instruction, no wait) stops IR passes sinking a load next to its
+// use, and the scheduling barrier stops the machine scheduler doing the same.
+__device__ __forceinline__ void pin_issue_order() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, int G, bool kPageTile, int NBUF, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodeParams p) {
   constexpr int KS = D / 32;      // MFMA k-steps per tile = V loads per lane per tile
   constexpr int LPV = D / 8;      // lanes per token in the V layout
@@ -67,8 +90,11 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   static_assert(TPV * KS == kTile, "tile shape");
   constexpr int HG = (G + 3) / 4; // 16-lane rows that hold real heads in the score layout
 
-  __shared__ float4 sm_p[kWaves][HG][kTile];
-  __shared__ float4 sm_alpha[kWaves][HG];
+  constexpr int KPITCH = D * 2 + 16;   // bytes per K row in LDS (16-B pad: conflict-free MFMA reads)
+  __shared__ int sm_pid[kSegPages];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k[kWaves][kTile * KPITCH];
+  __shared__ f32x4 sm_p[kWaves][HG][kTile];
+  __shared__ f32x4 sm_alpha[kWaves][HG];
   __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
   __shared__ float sm_acc[kWaves][G][D];
 
@@ -77,24 +103,36 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int log2P = p.page_log2;
   const int pmask = (1 << log2P) - 1;
+  const int32_t *pt = p.page_table + size_t(b) * p.max_pages;
+  const int t0 = s * p.chunk;
+
+  // Page ids of the first segment are fetched together with the sequence
+  // length (the chunk is known on the host; entries past the sequence's end
+  // are read but never used).
+  const int pg0 = t0 >> log2P;
+  auto fetch_pids = [&](int pga, int npg) {
+    for (int i = threadIdx.x; i < npg; i += kWaves * 64) sm_pid[i] = pt[min(pga + i, p.max_pages - 1)];
+  };
+  const int chunk_pages = (p.chunk + pmask) >> log2P;
+  fetch_pids(pg0, min(chunk_pages, kSegPages));
 
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.max_pages << log2P);
-  const int t0 = s * p.chunk;
   const int t1 = min(t0 + p.chunk, L);
-  const int ntiles = t1 > t0 ? (t1 - t0 + kTile - 1) / kTile : 0;
-  const int my_tiles = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
   // q rows of the group as the MFMA A operand: lane = head (lane & 15), dims 32j + 8(lane >> 4)
   const int qh = lane & 15, qk = lane >> 4;
   bf16x8 qa[KS];
 #pragma unroll
   for (int j = 0; j < KS; ++j) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (qh < G)
-      w = *reinterpret_cast<const uint4 *>(p.q + (size_t(b) * p.Hq + size_t(g) * G + qh) * D + 32 * j + 8 * qk);
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (qh < G) w = ld16(p.q + (size_t(b) * p.Hq + size_t(g) * G + qh) * D + 32 * j + 8 * qk);
     qa[j] = as_bf16x8(w);
   }
+  // Make q resident now: otherwise the first use inside the pipelined loop
+  // would make the compiler wait for every load in flight.
+#pragma unroll
+  for (int j = 0; j < KS; ++j) asm volatile("" ::"v"(qa[j]));
 
   float m[4], ls[4];
 #pragma unroll
@@ -108,123 +146,149 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
 
-  const int32_t *pt = p.page_table + size_t(b) * p.max_pages;
   const size_t row_stride = size_t(p.Hkv) * D;
-  const uint16_t *kbase = p.k_pool + size_t(g) * D + 8 * qk;
+  // K and V are both read as whole rows: lane = 8 dims (lane % LPV) of token
+  // slot lane / LPV; 4 (D=128) or 8 (D=64) full rows per load instruction.
+  const uint16_t *kbase = p.k_pool + size_t(g) * D + 8 * (lane % LPV);
   const uint16_t *vbase = p.v_pool + size_t(g) * D + 8 * (lane % LPV);
   const int vt = lane / LPV;
-  const int last = t1 - 1;
 
-  struct Pids { int k; int v[KS]; };
-  struct Regs { uint4 k[KS]; uint4 v[KS]; };
+  struct Regs { u32x4 k[KS]; u32x4 v[KS]; int pid; };
 
-  auto tile_base = [&](int k) { return t0 + kTile * (wave + kWaves * k); };
+  // Segments of at most kSegPages pages: their page ids sit in LDS while the
+  // four waves stream the segment's tiles (each wave a contiguous range).
+  for (int sa = t0; sa < t1;) {
+    const int pga = sa >> log2P;
+    const int sb = min(t1, (pga + kSegPages) << log2P);
+    if (sa != t0) {
+      __syncthreads();
+      fetch_pids(pga, min(((sb - 1) >> log2P) - pga + 1, kSegPages));
+    }
+    __syncthreads();
 
-  auto load_pids = [&](int k, Pids &pi) {
-    const int tb = tile_base(k);
-    pi.k = pt[min(tb + (lane & 15), last) >> log2P];
-    if constexpr (!kPageTile) {
-#pragma unroll
-      for (int i = 0; i < KS; ++i) pi.v[i] = pt[min(tb + TPV * i + vt, last) >> log2P];
-    }
-  };
+    const int nst = (sb - sa + kTile - 1) / kTile;
+    const int tpw = (nst + kWaves - 1) / kWaves;
+    const int first = min(wave * tpw, nst);
+    const int my_tiles = min(tpw, nst - first);
+    const int last = sb - 1;
+    const int tw0 = sa + kTile * first;   // first token of this wave's range
 
-  auto load_kv = [&](int k, const Pids &pi, Regs &rg) {
-    const int tb = tile_base(k);
-    {
-      const int pid = unsigned(pi.k) < unsigned(p.num_pages) ? pi.k : 0;
-      const size_t row = (size_t(pid) << log2P) + (min(tb + (lane & 15), last) & pmask);
-      const uint4 *kp = reinterpret_cast<const uint4 *>(kbase + row * row_stride);
+    auto load_kv = [&](int k, Regs &rg) {
+      const int tb = tw0 + kTile * k;
+      if constexpr (kPageTile) {
+        const int raw = __builtin_amdgcn_readfirstlane(sm_pid[(min(tb, last) >> log2P) - pga]);
+        rg.pid = raw;
+        const int pid = unsigned(raw) < unsigned(p.num_pages) ? raw : 0;
+        const size_t page_row = size_t(pid) << log2P;
 #pragma unroll
-      for (int j = 0; j < KS; ++j) rg.k[j] = kp[4 * j];
-    }
+        for (int i = 0; i < KS; ++i) {
+          const size_t row = page_row + (min(tb + TPV * i + vt, last) & pmask);
+          rg.k[i] = ld16(kbase + row * row_stride);
+          rg.v[i] = ld16(vbase + row * row_stride);
+        }
+      } else {
+        rg.pid = sm_pid[(min(tb + (lane & 15), last) >> log2P) - pga];   // page of this lane's score token
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      const int raw = kPageTile ? pi.k : pi.v[i];
-      const int pid = unsigned(raw) < unsigned(p.num_pages) ? raw : 0;
-      const size_t row = (size_t(pid) << log2P) + (min(tb + TPV * i + vt, last) & pmask);
-      rg.v[i] = *reinterpret_cast<const uint4 *>(vbase + row * row_stride);
-    }
-  };
+        for (int i = 0; i < KS; ++i) {
+          const int tv = min(tb + TPV * i + vt, last);
+          const int rv = sm_pid[(tv >> log2P) - pga];
+          const int pv = unsigned(rv) < unsigned(p.num_pages) ? rv : 0;
+          const size_t row = (size_t(pv) << log2P) + (tv & pmask);
+          rg.k[i] = ld16(kbase + row * row_stride);
+          rg.v[i] = ld16(vbase + row * row_stride);
+        }
+      }
+    };
 
-  auto compute = [&](int k, const Pids &pi, const Regs &rg) {
-    const int tb = tile_base(k);
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int k, const Regs &rg, bool active) {
+      const int tb = tw0 + kTile * k;
+      // re-lay K from whole rows into the B operand (lane = token, 8 dims per k-step)
+      unsigned char *kt = sm_k[wave];
+      wave_lds_sync();
 #pragma unroll
-    for (int j = 0; j < KS; ++j) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(rg.k[j]), c, 0, 0, 0);
-    // this lane: token tb + (lane & 15), heads 4 * (lane >> 4) + r
-    const bool valid = tb + (lane & 15) < t1;
-    const bool bad = unsigned(pi.k) >= unsigned(p.num_pages);
-    float alpha[4], pr[4];
+      for (int i = 0; i < KS; ++i)
+        *reinterpret_cast<u32x4 *>(kt + (TPV * i + vt) * KPITCH + 16 * (lane % LPV)) = rg.k[i];
+      wave_lds_sync();
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x = !valid ? -INFINITY : (bad ? NAN : c[r] * p.scale_log2);
-      const float mn = fmaxf(m[r], row_max16(x));
-      alpha[r] = (m[r] == mn) ? 1.f : fast_exp2(m[r] - mn);
-      pr[r] = fast_exp2(x - mn);
-      ls[r] = fmaf(ls[r], alpha[r], pr[r]);
-      m[r] = mn;
-    }
-    // hand p (and the rescale factors) over to the V layout
-    wave_lds_sync();
-    if (lane < 16 * HG) {
-      sm_p[wave][lane >> 4][lane & 15] = make_float4(pr[0], pr[1], pr[2], pr[3]);
-      if ((lane & 15) == 0) sm_alpha[wave][lane >> 4] = make_float4(alpha[0], alpha[1], alpha[2], alpha[3]);
-    }
-    wave_lds_sync();
-    float al[HG * 4];
+      for (int j = 0; j < KS; ++j) {
+        const u32x4 kb = ld16(kt + (lane & 15) * KPITCH + 16 * (4 * j + qk));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(kb), c, 0, 0, 0);
+      }
+      // this lane: token tb + (lane & 15), heads 4 * (lane >> 4) + r
+      const bool valid = active && tb + (lane & 15) <= last;
+      const bool bad = unsigned(rg.pid) >= unsigned(p.num_pages);
+      float alpha[4], pr[4];
 #pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      const float4 a = sm_alpha[wave][hg];
-      al[4 * hg] = a.x; al[4 * hg + 1] = a.y; al[4 * hg + 2] = a.z; al[4 * hg + 3] = a.w;
-    }
-    bool moved = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) moved |= (al[h] != 1.f);
-    if (moved) {   // wave-uniform: every lane read the same factors
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[h][d] *= al[h];
-    }
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      float ph[HG * 4];
+      for (int r = 0; r < 4; ++r) {
+        const float x = !valid ? -INFINITY : (bad ? NAN : c[r] * p.scale_log2);
+        const float mn = fmaxf(m[r], row_max16(x));
+        alpha[r] = (m[r] == mn) ? 1.f : fast_exp2(m[r] - mn);
+        pr[r] = fast_exp2(x - mn);
+        ls[r] = fmaf(ls[r], alpha[r], pr[r]);
+        m[r] = mn;
+      }
+      // hand p (and the rescale factors) over to the V layout
+      wave_lds_sync();
+      if (lane < 16 * HG) {
+        sm_p[wave][lane >> 4][lane & 15] = f32x4{pr[0], pr[1], pr[2], pr[3]};
+        if ((lane & 15) == 0) sm_alpha[wave][lane >> 4] = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
+      }
+      wave_lds_sync();
+      float al[HG * 4];
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
-        const float4 q4 = sm_p[wave][hg][TPV * i + vt];
-        ph[4 * hg] = q4.x; ph[4 * hg + 1] = q4.y; ph[4 * hg + 2] = q4.z; ph[4 * hg + 3] = q4.w;
+        const f32x4 a = sm_alpha[wave][hg];
+        al[4 * hg] = a[0]; al[4 * hg + 1] = a[1]; al[4 * hg + 2] = a[2]; al[4 * hg + 3] = a[3];
       }
-      float vf[8];
-      unpack8(rg.v[i], vf);
+      bool moved = false;
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h) moved |= (al[h] != 1.f);
+      if (moved) {   // wave-uniform: every lane read the same factors
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc[h][d] = fmaf(ph[h], vf[d], acc[h][d]);
-    }
-  };
-
-  if (my_tiles > 0) {
-    Pids pa, pb;
-    Regs ra, rb;
-    load_pids(0, pa);
-    load_kv(0, pa, ra);
-    if (my_tiles > 1) load_pids(1, pb);
-    for (int k = 0; k < my_tiles; k += 2) {
-      // tile k is in ra; pids of tile k + 1 are in pb
-      if (k + 1 < my_tiles) {
-        load_kv(k + 1, pb, rb);
-        if (k + 2 < my_tiles) load_pids(k + 2, pa);
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[h][d] *= al[h];
       }
-      compute(k, pa, ra);
-      if (k + 1 < my_tiles) {
-        if (k + 2 < my_tiles) {
-          load_kv(k + 2, pa, ra);
-          if (k + 3 < my_tiles) load_pids(k + 3, pb);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        float ph[HG * 4];
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) {
+          const f32x4 q4 = sm_p[wave][hg][TPV * i + vt];
+          ph[4 * hg] = q4[0]; ph[4 * hg + 1] = q4[1]; ph[4 * hg + 2] = q4[2]; ph[4 * hg + 3] = q4[3];
         }
-        compute(k + 1, pb, rb);
+        float vf[8];
+        unpack8v(rg.v[i], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) acc[h][d] = fmaf(ph[h], vf[d], acc[h][d]);
+      }
+    };
+
+    // Ring of NBUF register tiles: NBUF-1 tiles are in flight while one is
+    // computed.  The body is branch-free: loads past the range repeat the last
+    // tile (cache hits) and their compute is fully masked, so the compiler
+    // can neither sink a prefetch next to its use nor merge waits across paths.
+    if (my_tiles > 0) {
+      const int lt = my_tiles - 1;
+      Regs rg[NBUF];
+#pragma unroll
+      for (int j = 0; j < NBUF - 1; ++j) {
+        load_kv(min(j, lt), rg[j]);
+        pin_issue_order();
+      }
+      for (int k = 0; k < my_tiles; k += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          load_kv(min(k + u + NBUF - 1, lt), rg[(u + NBUF - 1) % NBUF]);
+          pin_issue_order();
+          compute(k + u, rg[u], k + u < my_tiles);
+        }
       }
     }
+    sa = sb;
   }
 
   // ---- per-wave totals: sums over the score rows and over the V token slots
@@ -254,7 +318,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   }
   __syncthreads();
 
-  // ---- merge the waves (ascending order) and write this split's partial
+  // ---- merge the waves (ascending order = ascending positions) and write the partial
   for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
@@ -279,14 +343,20 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   }
 }
 
+template <int D, int G, int W>
+hipError_t launch_mfma_w(const DecodeParams &p, hipStream_t stream) {
+  const dim3 grid{unsigned(p.num_splits), unsigned(p.Hkv), unsigned(p.B)}, block{W * 64};
+  constexpr int NBUF = D == 128 ? 3 : 4;
+  if (p.page_log2 >= 4)
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, W>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false, NBUF, W>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t launch_mfma(const DecodeParams &p, hipStream_t stream) {
-  const dim3 grid{unsigned(p.num_splits), unsigned(p.Hkv), unsigned(p.B)}, block{kWaves * 64};
-  if (p.page_log2 >= 4)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false>), grid, block, 0, stream, p);
-  return hipGetLastError();
+  return p.waves == 8 ? launch_mfma_w<D, G, 8>(p, stream) : launch_mfma_w<D, G, 4>(p, stream);
 }
 
 }  // namespace
