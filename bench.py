@@ -93,7 +93,7 @@ def main():
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.layers - 1)]
     B, Hq, Hkv, D, P = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.P
     max_len = inp.max_seq_len
-    S = args.splits or pkv.num_splits(B, Hkv, max_len, P)
+    S = args.splits or pkv.num_splits(B, Hq, Hkv, max_len, P, int(inp.seq_lens.sum()))
     o_p, l_p = pkv.workspace(B, Hq, D, S, dev)
     out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     log(f"[bench] num_splits {S}, chunk {pkv.split_chunk(max_len, S, P)}, layers {args.layers}")

@@ -95,7 +95,8 @@ pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t p
  * lse = -inf.  Every element of o_partial / lse_partial is written.
  *
  *   head_dim D in {64, 128}; group Hq/Hkv in {1, 2, 4, 8}; page_size a power of
- *   two in [1, 1024]; num_splits in [1, 1024]; max_seq_len in [0, max_pages_per_seq*page_size].
+ *   two in [1, 1024]; num_splits in [1, 1024]; max_seq_len in [0, max_pages_per_seq*page_size];
+ *   num_splits * Hkv * B < 2^31 (the workgroup count).
  *   q, k_pool, v_pool 16-byte aligned (else PKV_ERR_ALIGN).
  * Preconditions (device): seq_lens[b] <= max_seq_len.  Positions past
  * num_splits*chunk are not visited.  A page id outside [0, num_pages) makes
@@ -130,14 +131,23 @@ pkv_status pkv_decode_merge(const float *o_partial, const float *lse_partial, in
  *
  * The pages only say the launcher does the split-K arithmetic and that small
  * batches underfill the GPU despite split-KV (AstrAI "CUDA Kernels", sections
- * "File Layout" and "Known Optimization Targets"); the rule is a reading:
- *     S_fill = ceil(2*num_cus / (B*Hkv))     enough workgroups to fill the GPU
- *     S_bal  = ceil(max_seq_len / 2048)      splits of at most 2048 positions
- *     S      = clamp(max(S_fill, S_bal), 1, max(1, ceil(max_seq_len / 256)))
- * Returns >= 1 for valid arguments, PKV_ERR_SHAPE otherwise.
+ * "File Layout" and "Known Optimization Targets"); the rule is a reading,
+ * tuned by measurement on MI355X:
+ *     streams = B * Hkv                         one workgroup each per split
+ *     S_fill  = ceil(w * num_cus / streams)     w = 2 if Hq/Hkv >= 8, else 1
+ *     ragged  = total_tokens < 0 (unknown) or total_tokens < 0.9 * B * max_seq_len
+ *     S       = ragged ? max(S_fill, ceil(max_seq_len / 2048)) : S_fill
+ *     S       = clamp(S, 1, min(1024, max(1, ceil(max_seq_len / 256))))
+ * total_tokens is the sum of the batch's sequence lengths when the caller
+ * knows it (a serving scheduler does), else any negative value.  Uniform
+ * batches keep one split per (sequence, kv head) while that fills the GPU;
+ * ragged ones are cut into splits of at most 2048 positions, so that the
+ * workgroups of long sequences are not the last to finish.
+ * Returns >= 1 for valid arguments, PKV_ERR_SHAPE otherwise (B, Hkv or num_cus
+ * below 1, Hq not a multiple of Hkv, page_size not a power of two).
  */
-int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
-                       int32_t num_cus);
+int32_t pkv_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
+                       int64_t total_tokens, int32_t page_size, int32_t num_cus);
 
 /* pkv_split_chunk -- positions covered by one split: the smallest multiple of
  * page_size >= ceil(max_seq_len / num_splits).  0 if max_seq_len == 0,

@@ -55,14 +55,19 @@ int32_t pkv_split_chunk(int32_t max_seq_len, int32_t num_splits, int32_t page_si
   return int32_t(ceil_div(per, page_size) * page_size);
 }
 
-int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
-                       int32_t num_cus) {
-  if (B < 1 || Hkv < 1 || max_seq_len < 0 || !is_pow2(page_size) || num_cus < 1)
+int32_t pkv_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
+                       int64_t total_tokens, int32_t page_size, int32_t num_cus) {
+  if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || max_seq_len < 0 || !is_pow2(page_size) ||
+      num_cus < 1)
     return PKV_ERR_SHAPE;
-  const int64_t groups = int64_t(B) * Hkv;
-  const int64_t s_fill = ceil_div(2 * int64_t(num_cus), groups);
-  const int64_t s_bal = ceil_div(max_seq_len, 2048);
-  int64_t s = s_fill > s_bal ? s_fill : s_bal;
+  const int64_t streams = int64_t(B) * Hkv;          // (sequence, kv head) pairs
+  const int64_t wg_per_cu = Hq / Hkv >= 8 ? 2 : 1;   // workgroups that keep one CU busy
+  int64_t s = ceil_div(wg_per_cu * num_cus, streams);
+  const bool uniform = total_tokens >= 0 && total_tokens * 10 >= int64_t(B) * max_seq_len * 9;
+  if (!uniform) {
+    const int64_t s_bal = ceil_div(max_seq_len, 2048);
+    if (s_bal > s) s = s_bal;
+  }
   int64_t cap = ceil_div(max_seq_len, 256);
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;
@@ -109,6 +114,7 @@ pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *
   if (!is_pow2(page_size) || page_size > 1024) return PKV_ERR_UNSUPPORTED;
   if (int64_t(max_seq_len) > int64_t(max_pages_per_seq) * page_size) return PKV_ERR_SHAPE;
   if (B > 65535 || Hkv > 65535) return PKV_ERR_SHAPE;
+  if (int64_t(num_splits) * Hkv * B > int64_t(INT32_MAX)) return PKV_ERR_SHAPE;   // grid size
   if (int64_t(num_pages) * page_size > (int64_t(1) << 31)) return PKV_ERR_SHAPE;
   if (int64_t(max_pages_per_seq) * page_size > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return PKV_ERR_SHAPE;
@@ -136,7 +142,6 @@ pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *
   p.num_splits = num_splits;
   p.chunk = max_seq_len == 0 ? page_size : pkv_split_chunk(max_seq_len, num_splits, page_size);
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.waves = 4;
   hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -22,6 +22,13 @@
 //   sequence length); each wave streams a contiguous range of tiles through
 //   a ring of register buffers, with two (D=128) or three (D=64) tiles in
 //   flight while one is computed.
+//   K and V are read once, so their loads carry the non-temporal hint: on
+//   gfx950 this measured ~10% faster than default-policy loads of the same
+//   addresses (the lines are not kept in L2 / the memory-side cache).
+//   Workgroup order: kv head fastest, then sequence, then split.  With one
+//   split this keeps the kv heads of a sequence (which read the same pages)
+//   launched together; with several, every sequence's first split is
+//   dispatched before any second split, so long ragged sequences start early.
 #include <math.h>
 
 #include "pkv_device.h"
@@ -41,6 +48,10 @@ constexpr int kSegPages = 2048;  // page ids held in LDS at a time
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// streaming (non-temporal) 16-byte load for K/V rows, which are read exactly once
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ void unpack8v(const u32x4 &v, float f[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -100,7 +111,10 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // one-dimensional grid: kv head fastest, then sequence, then split
+  const int g = blockIdx.x % p.Hkv;
+  const int b = (blockIdx.x / p.Hkv) % p.B;
+  const int s = blockIdx.x / (p.Hkv * p.B);
   const int log2P = p.page_log2;
   const int pmask = (1 << log2P) - 1;
   const int32_t *pt = p.page_table + size_t(b) * p.max_pages;
@@ -183,8 +197,8 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
           const size_t row = page_row + (min(tb + TPV * i + vt, last) & pmask);
-          rg.k[i] = ld16(kbase + row * row_stride);
-          rg.v[i] = ld16(vbase + row * row_stride);
+          rg.k[i] = ld16_stream(kbase + row * row_stride);
+          rg.v[i] = ld16_stream(vbase + row * row_stride);
         }
       } else {
         rg.pid = sm_pid[(min(tb + (lane & 15), last) >> log2P) - pga];   // page of this lane's score token
@@ -194,8 +208,8 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
           const int rv = sm_pid[(tv >> log2P) - pga];
           const int pv = unsigned(rv) < unsigned(p.num_pages) ? rv : 0;
           const size_t row = (size_t(pv) << log2P) + (tv & pmask);
-          rg.k[i] = ld16(kbase + row * row_stride);
-          rg.v[i] = ld16(vbase + row * row_stride);
+          rg.k[i] = ld16_stream(kbase + row * row_stride);
+          rg.v[i] = ld16_stream(vbase + row * row_stride);
         }
       }
     };
@@ -343,20 +357,16 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   }
 }
 
-template <int D, int G, int W>
-hipError_t launch_mfma_w(const DecodeParams &p, hipStream_t stream) {
-  const dim3 grid{unsigned(p.num_splits), unsigned(p.Hkv), unsigned(p.B)}, block{W * 64};
-  constexpr int NBUF = D == 128 ? 3 : 4;
-  if (p.page_log2 >= 4)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, W>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false, NBUF, W>), grid, block, 0, stream, p);
-  return hipGetLastError();
-}
-
 template <int D, int G>
 hipError_t launch_mfma(const DecodeParams &p, hipStream_t stream) {
-  return p.waves == 8 ? launch_mfma_w<D, G, 8>(p, stream) : launch_mfma_w<D, G, 4>(p, stream);
+  constexpr int kWaves = 4;
+  const dim3 grid{unsigned(p.num_splits * p.Hkv * p.B)}, block{kWaves * 64};
+  constexpr int NBUF = D == 128 ? 3 : 4;
+  if (p.page_log2 >= 4)
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, kWaves>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false, NBUF, kWaves>), grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -21,7 +21,6 @@ struct DecodeParams {
   int num_pages, max_pages;
   int num_splits, chunk;     // split s covers [s*chunk, (s+1)*chunk)
   float scale_log2;          // softmax scale * log2(e)
-  int waves;                 // waves per workgroup of the matrix-core kernel (4 or 8)
 };
 
 hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,

@@ -39,10 +39,12 @@ def num_cus(device=None) -> int:
     return _num_cus_cache[key]
 
 
-def num_splits(B: int, Hkv: int, max_seq_len: int, page_size: int, n_cus: int | None = None) -> int:
-    """The split-count heuristic of the library (host only)."""
+def num_splits(B: int, Hq: int, Hkv: int, max_seq_len: int, page_size: int,
+               total_tokens: int = -1, n_cus: int | None = None) -> int:
+    """The split-count heuristic of the library (host only).  ``total_tokens``
+    is the sum of the sequence lengths if known (-1: unknown, treated as ragged)."""
     n_cus = num_cus() if n_cus is None else n_cus
-    s = lib().pkv_num_splits(B, Hkv, max_seq_len, page_size, n_cus)
+    s = lib().pkv_num_splits(B, Hq, Hkv, max_seq_len, total_tokens, page_size, n_cus)
     check(min(s, 0), "pkv_num_splits")
     return s
 
@@ -100,12 +102,13 @@ def workspace(B: int, Hq: int, D: int, splits: int, device) -> tuple[torch.Tenso
 
 def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
                       splits: int | None = None, scale: float | None = None,
-                      o_partial=None, lse_partial=None):
+                      o_partial=None, lse_partial=None, total_tokens: int = -1):
     """Split-KV attention over the paged pool; returns (o_partial, lse_partial).
 
     q ``[B,Hq,D]`` bf16; pools ``[num_pages,P,Hkv,D]`` bf16; page_table int32
     ``[B,max_pages]``; seq_lens int32 ``[B]``; ``max_seq_len`` is a host bound
-    on ``seq_lens`` (no device read)."""
+    on ``seq_lens`` (no device read); ``total_tokens`` (sum of ``seq_lens``, if
+    the caller knows it) only steers the split heuristic when ``splits`` is None."""
     _on_gpu(q, k_pool, v_pool, page_table, seq_lens)
     _require(q.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
              "q and the pools must be bfloat16")
@@ -118,7 +121,7 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
     B, Hq, D = q.shape
     num_pages, P, Hkv, D2 = k_pool.shape
     _require(D2 == D and page_table.shape[0] == B and seq_lens.shape == (B,), "inconsistent shapes")
-    S = num_splits(B, Hkv, max_seq_len, P) if splits is None else splits
+    S = num_splits(B, Hq, Hkv, max_seq_len, P, total_tokens) if splits is None else splits
     if o_partial is None or lse_partial is None:
         o_partial, lse_partial = workspace(B, Hq, D, S, q.device)
     _require(o_partial.shape == (B, Hq, S, D) and o_partial.dtype == torch.float32 and o_partial.is_contiguous(),
@@ -159,10 +162,11 @@ def decode_merge(o_partial, lse_partial, out=None, lse_out=None, want_lse: bool 
 
 def decode_step(q, k_new, v_new, k_pool, v_pool, page_table, seq_lens, slot_mapping,
                 max_seq_len: int, splits: int | None = None, out=None, ws=None,
-                want_lse: bool = False):
+                want_lse: bool = False, total_tokens: int = -1):
     """One decode step: store the new rows, split-KV attention, merge."""
     kv_store(k_pool, v_pool, k_new, v_new, slot_mapping)
     o_p, l_p = paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits,
                                  o_partial=None if ws is None else ws[0],
-                                 lse_partial=None if ws is None else ws[1])
+                                 lse_partial=None if ws is None else ws[1],
+                                 total_tokens=total_tokens)
     return decode_merge(o_p, l_p, out=out, want_lse=want_lse)

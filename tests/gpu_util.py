@@ -54,7 +54,8 @@ class DeviceStep:
 
     def attend(self, splits=None, want_lse=False):
         o_p, l_p = pkv.paged_decode_attn(self.q, self.k_pool, self.v_pool, self.page_table,
-                                         self.seq_lens, self.inp.max_seq_len, splits)
+                                         self.seq_lens, self.inp.max_seq_len, splits,
+                                         total_tokens=int(self.inp.seq_lens.sum()))
         res = pkv.decode_merge(o_p, l_p, want_lse=want_lse)
         return res, o_p, l_p
 

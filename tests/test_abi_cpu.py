@@ -42,23 +42,32 @@ def test_status_strings(lib):
 
 
 def test_split_heuristic_on_the_five_workloads(lib):
-    # B, Hkv, max_seq_len, page_size -> S at 256 CUs
-    cases = {(2, 1, 100, 16): 1, (32, 8, 4096, 16): 2, (64, 8, 8192, 16): 4,
-             (4, 8, 65536, 16): 32, (128, 16, 2048, 1): 1}
+    # B, Hq, Hkv, max_seq_len, total_tokens, page_size -> S at 256 CUs
+    cases = {(2, 4, 1, 100, 137, 16): 1,            # tiny, ragged: capped by ceil(100 / 256)
+             (32, 32, 8, 4096, 32 * 4096, 16): 1,   # uniform: 256 streams fill 256 CUs
+             (64, 32, 8, 8192, 281358, 16): 4,      # ragged: splits of at most 2048 positions
+             (4, 64, 8, 65536, 4 * 65536, 16): 16,  # uniform, G = 8: two workgroups per CU
+             (128, 16, 16, 2048, 128 * 2048, 1): 1}
     for args, s in cases.items():
         assert lib.pkv_num_splits(*args, 256) == s, args
+    # the same shapes without a token count are treated as ragged
+    assert lib.pkv_num_splits(32, 32, 8, 4096, -1, 16, 256) == 2
+    assert lib.pkv_num_splits(4, 64, 8, 65536, -1, 16, 256) == 32
 
 
 def test_split_heuristic_properties(lib):
     for B in [1, 3, 32, 500]:
-        for Hkv in [1, 8]:
+        for Hq, Hkv in [(1, 1), (8, 1), (32, 8), (64, 8)]:
             for L in [0, 1, 255, 256, 2049, 100000]:
-                s = lib.pkv_num_splits(B, Hkv, L, 16, 256)
-                assert 1 <= s <= max(1, -(-L // 256))
-                if L > 0:
-                    assert s >= -(-L // 2048) or s == max(1, -(-L // 256))
-    assert lib.pkv_num_splits(0, 8, 10, 16, 256) == SHAPE
-    assert lib.pkv_num_splits(1, 8, 10, 12, 256) == SHAPE
+                cap = max(1, -(-L // 256))
+                for total in [-1, B * L, B * L // 2]:
+                    s = lib.pkv_num_splits(B, Hq, Hkv, L, total, 16, 256)
+                    assert 1 <= s <= min(cap, 1024)
+                    if L > 0 and (total < 0 or 10 * total < 9 * B * L):
+                        assert s >= min(-(-L // 2048), cap)
+    assert lib.pkv_num_splits(0, 8, 8, 10, -1, 16, 256) == SHAPE
+    assert lib.pkv_num_splits(1, 8, 8, 10, -1, 12, 256) == SHAPE
+    assert lib.pkv_num_splits(1, 12, 8, 10, -1, 16, 256) == SHAPE
 
 
 def test_split_chunk_agrees_with_the_oracle_reading(lib):

@@ -40,7 +40,8 @@ def _oracle_full(inp):
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_decode_step_matches_oracle(gpu_device, cid):
     inp = inputs(cid)
-    S = pkv.num_splits(inp.cfg.B, inp.cfg.Hkv, inp.max_seq_len, inp.cfg.P)
+    S = pkv.num_splits(inp.cfg.B, inp.cfg.Hq, inp.cfg.Hkv, inp.max_seq_len, inp.cfg.P,
+                       int(inp.seq_lens.sum()))
     print(f"decode step cfg {cid} ({inp.cfg.describe()}), num_splits {S}", flush=True)
     st = DeviceStep(inp, gpu_device)
     (out, lse), o_p, l_p = st.step(want_lse=True)
@@ -60,9 +61,9 @@ def test_decode_step_matches_oracle(gpu_device, cid):
 def test_partials_match_oracle_split_mode(gpu_device, cid):
     inp = inputs(cid)
     cfg = inp.cfg
-    S = pkv.num_splits(cfg.B, cfg.Hkv, inp.max_seq_len, cfg.P)
-    if cid == 1:
-        S = 3  # force several splits on the tiny case
+    S = pkv.num_splits(cfg.B, cfg.Hq, cfg.Hkv, inp.max_seq_len, cfg.P, int(inp.seq_lens.sum()))
+    if cid in (1, 2):
+        S = 3 if cid == 1 else 2  # force several splits where the heuristic picks one
     st = DeviceStep(inp, gpu_device)
     st.store()
     _, o_p, l_p = st.attend(splits=S)
