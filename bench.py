@@ -27,6 +27,29 @@ import numpy as np
 
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
 
+# HBM bytes per launch of the decode kernel on the default workload, counted by
+# rocprofv3 in two runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
+# scaled by what the same counter reads for a 1 GiB device-to-device copy
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Keyed by the sha256 of the kernel's
+# sources when the counters were taken: any edit to them voids the figure.
+COUNTED_TRAFFIC = {
+    "workload": "llama3_8b_decode",
+    "sources_sha256": "ab4f1e1011e52a0a785b7eb4c1d7493fa40c496ffdf56cfecd1c7be2c75c0067",
+    "read_bytes": 537580395,    # FETCH_SIZE 262507.5 KiB x (1 GiB / 524322.1 KiB)
+    "write_bytes": 532480,      # WRITE_SIZE 520.0 KiB x (1 GiB / 1048576.0 KiB)
+}
+KERNEL_SOURCES = ["pkv_decode_mfma.hip", "pkv_device.h", "pkv_launch.h"]
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    from pathlib import Path
+    h = hashlib.sha256()
+    csrc = Path(__file__).resolve().parent / "paged_kv_gqa_store_amd" / "csrc"
+    for name in KERNEL_SOURCES:
+        h.update((csrc / name).read_bytes())
+    return h.hexdigest()
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -64,8 +87,9 @@ def cpu_model() -> str:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the step would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: this decode step has no multi-GPU path. It would shard "
+              "by sequence or by kv head with no exchange, or by context with one all-gather of the "
+              "(o, lse) partials before the merge. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     os.environ["PKV_DECODE_KERNEL"] = args.kernel
@@ -133,6 +157,10 @@ def main():
     # bytes the attention kernel itself must move: K+V, q, page ids, partials written once
     attn_kernel_b = terms["kv"] + terms["q"] + terms["page_ids"] + terms["partials"] // 2
     attn_us = float(attn_ms.mean() * 1e3)
+    traffic = None
+    if (cfg.name == COUNTED_TRAFFIC["workload"] and args.splits is None and args.kernel == "mfma"
+            and COUNTED_TRAFFIC["sources_sha256"] == kernel_sources_sha256()):
+        traffic = COUNTED_TRAFFIC["read_bytes"] + COUNTED_TRAFFIC["write_bytes"]
     achieved = attn_kernel_b / (attn_us * 1e-6) / 1e9
     log(f"[bench] step {ms_per_step * 1e3:.1f} us (wall) | store {store_ms.mean() * 1e3:.1f} us | "
         f"attn {attn_us:.1f} us (median {np.median(attn_ms) * 1e3:.1f}) | merge {merge_ms.mean() * 1e3:.1f} us")
@@ -195,7 +223,7 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "algorithmic_bytes_per_launch": attn_kernel_b,
         },
     }

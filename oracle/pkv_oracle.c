@@ -28,7 +28,7 @@
  *            chunked softmax keeps a (max, denominator, accumulator) triple
  *            per chunk and merges them in one fixed order.
  *
- * Readings where the pages leave a step open (listed in the design doc):
+ * Readings where the pages leave a step open:
  *   pool layout [num_pages, page_size, Hkv, D] (rows of Hkv*D per slot);
  *   q head h reads kv head h / G;  split s of a sequence covers positions
  *   [s*chunk, min((s+1)*chunk, L)) with chunk = round_up(ceil(max_L/S), P);

@@ -165,6 +165,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   // slot lane / LPV; 4 (D=128) or 8 (D=64) full rows per load instruction.
   const uint16_t *kbase = p.k_pool + size_t(g) * D + 8 * (lane % LPV);
   const uint16_t *vbase = p.v_pool + size_t(g) * D + 8 * (lane % LPV);
+  const uint16_t *qrow = p.q + (size_t(b) * p.Hq + size_t(g) * G) * D + 8 * (lane % LPV);
   const int vt = lane / LPV;
 
   struct Regs { u32x4 k[KS]; u32x4 v[KS]; int pid; };
@@ -187,8 +188,15 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
     const int last = sb - 1;
     const int tw0 = sa + kTile * first;   // first token of this wave's range
 
-    auto load_kv = [&](int k, Regs &rg) {
+    // Loads tile k (clamped into the range by the caller); when `real` is
+    // false the tile lies past the range and every lane reads the group's
+    // first q row instead: an L2 hit, where repeating a K/V tile would go to
+    // HBM again (lines loaded with the non-temporal hint are not retained).
+    auto load_kv = [&](int k, Regs &rg, bool real) {
       const int tb = tw0 + kTile * k;
+      const uint16_t *kb = real ? kbase : qrow;
+      const uint16_t *vb = real ? vbase : qrow;
+      const size_t rs = real ? row_stride : 0;
       if constexpr (kPageTile) {
         const int raw = __builtin_amdgcn_readfirstlane(sm_pid[(min(tb, last) >> log2P) - pga]);
         rg.pid = raw;
@@ -197,8 +205,8 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
           const size_t row = page_row + (min(tb + TPV * i + vt, last) & pmask);
-          rg.k[i] = ld16_stream(kbase + row * row_stride);
-          rg.v[i] = ld16_stream(vbase + row * row_stride);
+          rg.k[i] = ld16_stream(kb + row * rs);
+          rg.v[i] = ld16_stream(vb + row * rs);
         }
       } else {
         rg.pid = sm_pid[(min(tb + (lane & 15), last) >> log2P) - pga];   // page of this lane's score token
@@ -208,8 +216,8 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
           const int rv = sm_pid[(tv >> log2P) - pga];
           const int pv = unsigned(rv) < unsigned(p.num_pages) ? rv : 0;
           const size_t row = (size_t(pv) << log2P) + (tv & pmask);
-          rg.k[i] = ld16_stream(kbase + row * row_stride);
-          rg.v[i] = ld16_stream(vbase + row * row_stride);
+          rg.k[i] = ld16_stream(kb + row * rs);
+          rg.v[i] = ld16_stream(vb + row * rs);
         }
       }
     };
@@ -282,21 +290,21 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
     };
 
     // Ring of NBUF register tiles: NBUF-1 tiles are in flight while one is
-    // computed.  The body is branch-free: loads past the range repeat the last
-    // tile (cache hits) and their compute is fully masked, so the compiler
-    // can neither sink a prefetch next to its use nor merge waits across paths.
+    // computed.  The body is branch-free: loads past the range read a q row
+    // and their compute is fully masked, so the compiler can neither sink a
+    // prefetch next to its use nor merge waits across paths.
     if (my_tiles > 0) {
       const int lt = my_tiles - 1;
       Regs rg[NBUF];
 #pragma unroll
       for (int j = 0; j < NBUF - 1; ++j) {
-        load_kv(min(j, lt), rg[j]);
+        load_kv(min(j, lt), rg[j], j <= lt);
         pin_issue_order();
       }
       for (int k = 0; k < my_tiles; k += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
-          load_kv(min(k + u + NBUF - 1, lt), rg[(u + NBUF - 1) % NBUF]);
+          load_kv(min(k + u + NBUF - 1, lt), rg[(u + NBUF - 1) % NBUF], k + u + NBUF - 1 <= lt);
           pin_issue_order();
           compute(k + u, rg[u], k + u < my_tiles);
         }
