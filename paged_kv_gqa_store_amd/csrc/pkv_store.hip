@@ -5,14 +5,22 @@
 // 16-byte vectors when the row and its strides allow it.  The gfx950 design:
 //   - wave64; a row gets 2^k lanes (k chosen on the host so a 2 KB row is one
 //     wave and a 128 B row is 8 lanes: several short rows share a wave);
-//   - every lane issues all of its loads (K and V) before its first store, so
-//     each wave keeps 2 * units_per_lane 16-byte loads in flight;
+//   - a lane loads the row's slot index together with all of its K and V
+//     data (the data loads do not wait for the index), and stores only after
+//     the index is known to lie in the pool: each wave keeps
+//     2 * units_per_lane 16-byte loads in flight;
+//   - rows are read and written exactly once, so both directions carry the
+//     non-temporal hint (measured 2-7% faster on gfx950);
 //   - a slot outside the pool is skipped, so a bad index cannot fault.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 namespace {
+
+// Native vector types: the non-temporal builtins take no HIP struct vectors.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // Copies rows with UNITS (compile-time) copy units per lane, unit type U.
 // Row r of the inputs goes to pool row slots[r]; lanes_log2 lanes per row.
@@ -26,28 +34,28 @@ __global__ __launch_bounds__(256) void store_rows_kernel(
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t lane = gid & (lanes - 1);
   for (int64_t r = gid >> lanes_log2; r < n; r += rows_per_grid) {
-    const int64_t slot = slots[r];
-    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t slot = __builtin_nontemporal_load(slots + r);
     const U *ks = k_new + r * in_stride;
     const U *vs = v_new + r * in_stride;
-    U *kd = k_pool + slot * pool_stride;
-    U *vd = v_pool + slot * pool_stride;
     for (int64_t base = 0; base < row_units; base += UNITS * lanes) {
       U kb[UNITS], vb[UNITS];
 #pragma unroll
       for (int u = 0; u < UNITS; ++u) {
         const int64_t i = base + u * lanes + lane;
         if (i < row_units) {
-          kb[u] = ks[i];
-          vb[u] = vs[i];
+          kb[u] = __builtin_nontemporal_load(ks + i);
+          vb[u] = __builtin_nontemporal_load(vs + i);
         }
       }
+      if (slot < 0 || slot >= num_slots) continue;
+      U *kd = k_pool + slot * pool_stride;
+      U *vd = v_pool + slot * pool_stride;
 #pragma unroll
       for (int u = 0; u < UNITS; ++u) {
         const int64_t i = base + u * lanes + lane;
         if (i < row_units) {
-          kd[i] = kb[u];
-          vd[i] = vb[u];
+          __builtin_nontemporal_store(kb[u], kd + i);
+          __builtin_nontemporal_store(vb[u], vd + i);
         }
       }
     }
@@ -90,8 +98,8 @@ hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_
                            const int32_t *slots, int64_t n, int64_t row_b, int unit_b,
                            hipStream_t stream) {
   switch (unit_b) {
-    case 16: return launch_unit<uint4>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
-    case 8: return launch_unit<uint2>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
+    case 16: return launch_unit<u32x4>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
+    case 8: return launch_unit<u32x2>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
     case 4: return launch_unit<uint32_t>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
     case 2: return launch_unit<uint16_t>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
     default: return launch_unit<uint8_t>(k_pool, v_pool, num_slots, pool_stride_b, k_new, v_new, in_stride_b, slots, n, row_b, stream);
