@@ -83,6 +83,8 @@ def _load(path: Path | None = None):
         lib.oracle_paged_decode_split.restype = ctypes.c_int
         lib.oracle_merge.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p]
         lib.oracle_merge.restype = None
+        lib.oracle_indexing.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i64]
+        lib.oracle_indexing.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -126,6 +128,21 @@ def kv_store(k_pool, v_pool, k_new, v_new, slot_mapping, row_elems=None):
                                  row_elems * it)
     _check(rc, "kv_store")
     return k_out, v_out
+
+
+def indexing(weight, ids, start: int):
+    """Row gather of a vocabulary slice: ``weight`` is the slice ``[length, row]``
+    (any dtype), ``ids`` int32 ``[n]``; returns ``[n, row]`` with zero rows for
+    ids outside ``[start, start + length)``."""
+    weight = np.ascontiguousarray(weight)
+    assert weight.ndim == 2
+    ids = _c(ids, np.int32)
+    n = ids.shape[0]
+    out = np.empty((n, weight.shape[1]), weight.dtype)
+    out.view(np.uint8)[...] = 0xA5   # canary: a row the routine fails to write shows
+    _load().oracle_indexing(_ptr(out), _ptr(weight), weight.shape[0], weight.shape[1] * weight.itemsize,
+                            _ptr(ids), n, start)
+    return out
 
 
 def _problem(q, k_pool, v_pool, page_table, seq_lens):

@@ -27,6 +27,11 @@
  *   [merge]  cuDNN frontend "CSA Fused Compressor", section "ratio=128": a
  *            chunked softmax keeps a (max, denominator, accumulator) triple
  *            per chunk and merges them in one fixed order.
+ *   [index]  mini-sglang handbook, "Custom CUDA kernels", section "Moving
+ *            whole rows by index": the embedding lookup copies row
+ *            ids[t] - start of this rank's vocabulary slice to output row t,
+ *            and writes a row of zeros when the id lies outside the slice
+ *            [start, start + length) (vocabulary parallelism).
  *
  * Readings where the pages leave a step open:
  *   pool layout [num_pages, page_size, Hkv, D] (rows of Hkv*D per slot);
@@ -67,6 +72,20 @@ int oracle_kv_store(uint8_t *k_pool, uint8_t *v_pool, int64_t num_slots,
         memcpy(v_pool + slot * pool_row_stride, v_new + i * in_row_stride, (size_t)row_bytes);
     }
     return 0;
+}
+
+/* [index] Row gather with the vocabulary-slice mask: out row t is weight row
+ * ids[t] - start when start <= ids[t] < start + length, else all zero bytes.
+ * out is [n, row_bytes], weight is [length, row_bytes], both contiguous. */
+void oracle_indexing(uint8_t *out, const uint8_t *weight, int64_t length, int64_t row_bytes,
+                     const int32_t *ids, int64_t n, int64_t start) {
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t local = (int64_t)ids[t] - start;
+        if (local >= 0 && local < length)
+            memcpy(out + t * row_bytes, weight + local * row_bytes, (size_t)row_bytes);
+        else
+            memset(out + t * row_bytes, 0, (size_t)row_bytes);
+    }
 }
 
 /* [paged] Physical slot of logical position t of sequence b. */

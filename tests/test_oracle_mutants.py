@@ -32,6 +32,12 @@ MUTANTS = [
      "if (t1 > seq_lens[b]) t1 = seq_lens[b] - 1;"),
     ("bf16 widened wrongly", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     ("chunk not page aligned", "return (per + page_size - 1) / page_size * page_size;", "return per;"),
+    ("indexing ignores the slice start", "const int64_t local = (int64_t)ids[t] - start;",
+     "const int64_t local = (int64_t)ids[t];"),
+    ("indexing leaves masked rows unwritten", "memset(out + t * row_bytes, 0, (size_t)row_bytes);",
+     "(void)0;"),
+    ("indexing reads the mirrored row", "memcpy(out + t * row_bytes, weight + local * row_bytes",
+     "memcpy(out + t * row_bytes, weight + (length - 1 - local) * row_bytes"),
 ]
 
 PIN_CALLS = [
@@ -43,6 +49,9 @@ PIN_CALLS = [
     (pins.test_merge_closed_forms, ()),
     (pins.test_split_chunk_reading, ()),
     (pins.test_split_then_merge_equals_unsplit, (3,)),
+    (pins.test_indexing_matches_torch_embedding, ()),
+    (pins.test_indexing_shards_sum_to_the_full_lookup, ()),
+    (pins.test_indexing_closed_forms, ()),
 ] + [(pins.test_attention_matches_torch_sdpa_fp64, (c,)) for c in range(4)]
 
 

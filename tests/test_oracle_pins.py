@@ -298,3 +298,48 @@ def test_kv_bytes_of_the_five_workloads():
     assert W.kv_bytes([65536] * 4, 8, 128) == 1_073_741_824
     assert W.kv_bytes([2048] * 128, 16, 64) == 1_073_741_824
     assert W.kv_bytes([37, 100], 1, 64) == 35_072
+
+
+# ------------------------------------------------------------- indexing ----
+# mini-sglang handbook, "Custom CUDA kernels", section "Moving whole rows by
+# index": out[t] is row ids[t] - start of this rank's vocabulary slice, or a row
+# of zeros when ids[t] lies outside [start, start + length).
+
+def _index_case(vocab=97, row=24, n=300, seed=11):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    table = rng.standard_normal((vocab, row)).astype(np.float32)
+    ids = rng.integers(-5, vocab + 5, n).astype(np.int32)
+    return table, ids
+
+
+def test_indexing_matches_torch_embedding():
+    table, ids = _index_case()
+    start, length = 30, 40
+    shard = table[start:start + length]
+    got = oracle.indexing(shard, ids, start)
+    t_ids = torch.from_numpy(ids.astype(np.int64)) - start
+    valid = (t_ids >= 0) & (t_ids < length)
+    emb = torch.nn.functional.embedding(t_ids.clamp(0, length - 1), torch.from_numpy(shard))
+    ref = torch.where(valid[:, None], emb, torch.zeros(())).numpy()
+    assert got.tobytes() == ref.tobytes()
+
+
+def test_indexing_shards_sum_to_the_full_lookup():
+    """The zero rows exist so that the per-rank results add up (all-reduce) to
+    the lookup in the whole table: check that over a 4-way split of the vocabulary."""
+    table, ids = _index_case(vocab=100)
+    ids = np.clip(ids, 0, 99).astype(np.int32)
+    total = np.zeros((ids.shape[0], table.shape[1]), np.float32)
+    for start in range(0, 100, 25):
+        total += oracle.indexing(table[start:start + 25], ids, start)
+    assert total.tobytes() == table[ids].tobytes()
+
+
+def test_indexing_closed_forms():
+    table, _ = _index_case(vocab=50, row=3)
+    as_bytes = table.view(np.uint8).reshape(50, 12)[:, :6].copy()   # 6-byte rows
+    ids = np.array([7, 0, 49, 7, 21], np.int32)
+    assert oracle.indexing(as_bytes, ids, 0).tobytes() == as_bytes[ids].tobytes()
+    far = np.array([-1, 50, 1 << 30, -(1 << 30)], np.int32)
+    assert not oracle.indexing(as_bytes, far, 0).any()
+    assert oracle.indexing(as_bytes, np.zeros(0, np.int32), 0).shape == (0, 6)
