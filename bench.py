@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--store-reps", type=int, default=20, help="timed bulk-fill kv_store launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary measurements (embedding row gather)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size reference "
                          "for the HBM byte counters of a profiler run)")
@@ -82,6 +84,43 @@ def cpu_model() -> str:
     except OSError:
         pass
     return platform.processor() or "unknown"
+
+
+def time_launches(fn, reps: int, warmup: int = 3) -> float:
+    """Mean µs per call of ``fn`` over ``reps`` back-to-back calls, from HIP
+    events on the current stream (the stream the library launches on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def measure_extras(args, pkv, W, dev, to_bf16, to_i32) -> dict:
+    """Secondary rows of the path, each on its own synthetic workload."""
+    import torch
+    extras = {}
+    for name in ("llama3_8b_embed_prefill", "llama3_8b_embed_decode"):
+        icfg = W.INDEXING[name]
+        table, ids, start = W.make_indexing_inputs(icfg, rank=0)
+        t_d, ids_d = to_bf16(table), to_i32(ids)
+        out = torch.empty((icfg.n, icfg.hidden), dtype=torch.bfloat16, device=dev)
+        us = time_launches(lambda i: pkv.indexing(t_d, ids_d, start, out=out), reps=20)
+        nbytes = W.indexing_bytes(ids, start, table.shape[0], icfg.hidden * 2)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        extras[name] = {"op": "indexing", "us": round(us, 2), "GBps": round(gbps, 1),
+                        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "bytes": nbytes,
+                        "shape": f"slice {table.shape[0]}x{icfg.hidden} bf16 (1/{icfg.shards} of "
+                                 f"{icfg.vocab}), {icfg.n} ids"}
+        log(f"[bench] indexing {name}: {us:.1f} us, {gbps:.0f} GB/s ({gbps / PEAK_HBM_GBPS:.1%})")
+        del t_d, ids_d, out
+    return extras
 
 
 def main():
@@ -227,6 +266,9 @@ def main():
             "algorithmic_bytes_per_launch": attn_kernel_b,
         },
     }
+
+    if not args.no_extras:
+        result["extras"] = measure_extras(args, pkv, W, dev, to_bf16, to_i32)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)

@@ -3,6 +3,7 @@
  * over a paged KV cache, on AMD MI355X (gfx950).
  *
  *   pkv_kv_store          scatter the step's new K/V rows into the page pool
+ *   pkv_indexing          row gather from a vocabulary slice (embedding lookup)
  *   pkv_paged_decode_attn split-KV attention through the page table -> partials
  *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
  *   pkv_num_splits        split-count heuristic (host only)
@@ -74,6 +75,32 @@ pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t p
                         const void *k_new, const void *v_new, int64_t in_row_stride,
                         const int32_t *slot_mapping, int64_t n, int64_t row_elems,
                         int32_t elem_bytes, void *stream);
+
+/*
+ * pkv_indexing -- row gather from one rank's slice of a vocabulary-parallel
+ * embedding table.
+ *
+ * Follows: mini-sglang handbook, "Custom CUDA kernels", section "Moving whole
+ * rows by index" (the embedding lookup: output row t is the table row of
+ * token ids[t], or a row of zeros when the id falls outside this rank's slice
+ * of the vocabulary, so that an all-reduce over the ranks yields the lookup in
+ * the whole table).
+ *
+ *   out      device, [n, row_elems] contiguous; every row is written
+ *   weight   device, [length, row_elems] contiguous: vocabulary rows
+ *            start .. start + length - 1 (may be NULL when length == 0)
+ *   ids      device int32 [n]
+ *   elem_bytes 1, 2, 4 or 8
+ *     out[t] = weight[ids[t] - start]  if start <= ids[t] < start + length
+ *            = 0 (all bytes)           otherwise
+ * Rows move in the largest unit (16, 8, 4, 2, 1 bytes) dividing the row length
+ * and both base addresses.  Any id is safe: only in-slice rows are read.
+ * Returns PKV_OK (n == 0: nothing launched), PKV_ERR_NULL, PKV_ERR_SHAPE,
+ * PKV_ERR_UNSUPPORTED (elem_bytes), PKV_ERR_HIP.
+ */
+pkv_status pkv_indexing(void *out, const void *weight, int64_t length, int64_t row_elems,
+                        int32_t elem_bytes, const int32_t *ids, int64_t n, int64_t start,
+                        void *stream);
 
 /*
  * pkv_paged_decode_attn -- split-KV decode attention over the paged pool.

@@ -5,7 +5,10 @@ One decode step is three hand-written HIP kernels behind a C ABI
 
 * ``kv_store``           scatter the step's new K/V rows into the page pool;
 * ``paged_decode_attn``  split-KV attention over pages found through a page table;
-* ``decode_merge``       log-sum-exp merge of the split partials.
+* ``decode_merge``       log-sum-exp merge of the split partials;
+
+and ``indexing``, a row gather from one rank's slice of a vocabulary-parallel
+embedding table, on the same row-move kernel design as ``kv_store``.
 
 The binding in :mod:`paged_kv_gqa_store_amd.ops` only marshals arguments;
 PyTorch provides device memory and streams.  Loading the library is lazy, and
@@ -13,5 +16,6 @@ every op raises ``RuntimeError`` if ``libpkv.so`` is missing: there is no
 fallback implementation.
 """
 from .ops import (  # noqa: F401
-    decode_merge, decode_step, kv_store, num_splits, paged_decode_attn, split_chunk, workspace,
+    decode_merge, decode_step, indexing, kv_store, num_splits, paged_decode_attn, split_chunk,
+    workspace,
 )

@@ -98,6 +98,23 @@ pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t p
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+pkv_status pkv_indexing(void *out, const void *weight, int64_t length, int64_t row_elems,
+                        int32_t elem_bytes, const int32_t *ids, int64_t n, int64_t start,
+                        void *stream) {
+  if (n < 0 || length < 0 || row_elems < 0) return PKV_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return PKV_ERR_UNSUPPORTED;
+  if (n == 0 || row_elems == 0) return PKV_OK;
+  if (!out || !ids || (length > 0 && !weight)) return PKV_ERR_NULL;
+  if (length > (int64_t(1) << 40) || n > (int64_t(1) << 40)) return PKV_ERR_SHAPE;
+  const int64_t row_b = row_elems * elem_bytes;
+  const int unit = copy_unit({uint64_t(row_b), reinterpret_cast<uintptr_t>(out),
+                              reinterpret_cast<uintptr_t>(weight)});
+  hipError_t e = pkv::launch_gather_rows(out, weight, length, ids, n, start, row_b, unit,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool,
                                  const int32_t *page_table, const int32_t *seq_lens, int32_t B,
                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,

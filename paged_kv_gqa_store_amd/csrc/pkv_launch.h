@@ -28,6 +28,10 @@ hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_
                            const int32_t *slots, int64_t n, int64_t row_b, int unit_b,
                            hipStream_t stream);
 
+hipError_t launch_gather_rows(void *out, const void *weight, int64_t length, const int32_t *ids,
+                              int64_t n, int64_t start, int64_t row_b, int unit_b,
+                              hipStream_t stream);
+
 // Split-KV decode.  The matrix-core kernel runs by default; PKV_DECODE_KERNEL=valu
 // in the environment selects the all-VALU kernel instead (kept as the measured
 // baseline of that design choice; both honour the same contract).

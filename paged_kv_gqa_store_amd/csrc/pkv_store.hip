@@ -62,21 +62,89 @@ __global__ __launch_bounds__(256) void store_rows_kernel(
   }
 }
 
+// indexing: vocabulary-slice row gather (mini-sglang handbook, "Custom CUDA
+// kernels", section "Moving whole rows by index").  Output row r is row
+// ids[r] - start of the slice, or zeros when the id lies outside
+// [start, start + length).  Same lane layout as the store; the slice rows may
+// repeat across tokens, so they are loaded with the default cache policy,
+// while the output (written once) is stored non-temporally.
+template <typename U, int UNITS>
+__global__ __launch_bounds__(256) void gather_rows_kernel(
+    U *__restrict__ out, const U *__restrict__ weight, int64_t length,
+    const int32_t *__restrict__ ids, int64_t n, int64_t start, int64_t row_units,
+    int lanes_log2) {
+  const int64_t lanes = int64_t(1) << lanes_log2;
+  const int64_t rows_per_grid = (int64_t(gridDim.x) * blockDim.x) >> lanes_log2;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t lane = gid & (lanes - 1);
+  for (int64_t r = gid >> lanes_log2; r < n; r += rows_per_grid) {
+    const int64_t local = int64_t(__builtin_nontemporal_load(ids + r)) - start;
+    const bool valid = local >= 0 && local < length;
+    const U *src = weight + (valid ? local : 0) * row_units;
+    U *dst = out + r * row_units;
+    for (int64_t base = 0; base < row_units; base += UNITS * lanes) {
+      U buf[UNITS];
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u) {
+        const int64_t i = base + u * lanes + lane;
+        buf[u] = U{};
+        if (valid && i < row_units) buf[u] = src[i];
+      }
+#pragma unroll
+      for (int u = 0; u < UNITS; ++u) {
+        const int64_t i = base + u * lanes + lane;
+        if (i < row_units) __builtin_nontemporal_store(buf[u], dst + i);
+      }
+    }
+  }
+}
+
+// lanes per row (a power of two covering the row, at most one wave), copy units
+// per lane and grid size for n rows of row_units units
+struct RowLaunch {
+  int lanes_log2;
+  int64_t units_per_lane;
+  dim3 grid;
+};
+RowLaunch plan_rows(int64_t n, int64_t row_units) {
+  RowLaunch r;
+  r.lanes_log2 = 0;
+  while ((int64_t(1) << r.lanes_log2) < row_units && r.lanes_log2 < 6) ++r.lanes_log2;
+  const int64_t lanes = int64_t(1) << r.lanes_log2;
+  r.units_per_lane = (row_units + lanes - 1) / lanes;
+  const int64_t rows_per_block = 256 / lanes;
+  int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
+  // enough blocks to fill 256 CUs many times over; the grid-stride loop does the rest
+  if (blocks > 65536) blocks = 65536;
+  r.grid = dim3{unsigned(blocks)};
+  return r;
+}
+
+template <typename U>
+hipError_t launch_gather(void *out, const void *weight, int64_t length, const int32_t *ids,
+                         int64_t n, int64_t start, int64_t row_b, hipStream_t stream) {
+  const int64_t row_units = row_b / int64_t(sizeof(U));
+  const RowLaunch L = plan_rows(n, row_units);
+  U *o = static_cast<U *>(out);
+  const U *w = static_cast<const U *>(weight);
+  if (L.units_per_lane >= 2)
+    hipLaunchKernelGGL((gather_rows_kernel<U, 2>), L.grid, dim3{256}, 0, stream, o, w, length, ids,
+                       n, start, row_units, L.lanes_log2);
+  else
+    hipLaunchKernelGGL((gather_rows_kernel<U, 1>), L.grid, dim3{256}, 0, stream, o, w, length, ids,
+                       n, start, row_units, L.lanes_log2);
+  return hipGetLastError();
+}
+
 template <typename U>
 hipError_t launch_unit(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,
                        const void *k_new, const void *v_new, int64_t in_stride_b,
                        const int32_t *slots, int64_t n, int64_t row_b, hipStream_t stream) {
   const int64_t row_units = row_b / int64_t(sizeof(U));
-  // lanes per row: the power of two covering the row, at most one wave
-  int lanes_log2 = 0;
-  while ((int64_t(1) << lanes_log2) < row_units && lanes_log2 < 6) ++lanes_log2;
-  const int64_t lanes = int64_t(1) << lanes_log2;
-  const int64_t units_per_lane = (row_units + lanes - 1) / lanes;
-  const int64_t rows_per_block = 256 / lanes;
-  int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
-  // enough blocks to fill 256 CUs many times over; the grid-stride loop does the rest
-  if (blocks > 65536) blocks = 65536;
-  const dim3 grid{unsigned(blocks)}, block{256};
+  const RowLaunch L = plan_rows(n, row_units);
+  const int lanes_log2 = L.lanes_log2;
+  const int64_t units_per_lane = L.units_per_lane;
+  const dim3 grid = L.grid, block{256};
   U *kp = static_cast<U *>(k_pool);
   U *vp = static_cast<U *>(v_pool);
   const U *kn = static_cast<const U *>(k_new);
@@ -92,6 +160,18 @@ hipError_t launch_unit(void *k_pool, void *v_pool, int64_t num_slots, int64_t po
 }
 
 }  // namespace
+
+hipError_t launch_gather_rows(void *out, const void *weight, int64_t length, const int32_t *ids,
+                              int64_t n, int64_t start, int64_t row_b, int unit_b,
+                              hipStream_t stream) {
+  switch (unit_b) {
+    case 16: return launch_gather<u32x4>(out, weight, length, ids, n, start, row_b, stream);
+    case 8: return launch_gather<u32x2>(out, weight, length, ids, n, start, row_b, stream);
+    case 4: return launch_gather<uint32_t>(out, weight, length, ids, n, start, row_b, stream);
+    case 2: return launch_gather<uint16_t>(out, weight, length, ids, n, start, row_b, stream);
+    default: return launch_gather<uint8_t>(out, weight, length, ids, n, start, row_b, stream);
+  }
+}
 
 hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,
                            const void *k_new, const void *v_new, int64_t in_stride_b,

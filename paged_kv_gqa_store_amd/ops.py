@@ -94,6 +94,27 @@ def kv_store(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor, v_
     check(st, "pkv_kv_store")
 
 
+def indexing(weight: torch.Tensor, ids: torch.Tensor, start: int = 0, out=None) -> torch.Tensor:
+    """Embedding lookup in one rank's vocabulary slice: ``out[t] = weight[ids[t] - start]``,
+    or a zero row when ``ids[t]`` lies outside ``[start, start + weight.shape[0])``.
+
+    ``weight`` ``[length, row]`` contiguous (any dtype); ``ids`` int32 ``[n]``;
+    returns ``[n, row]`` of ``weight``'s dtype."""
+    _on_gpu(weight, ids)
+    _require(weight.dim() == 2 and weight.is_contiguous(), "weight must be a contiguous 2-D table")
+    _require(ids.dtype == torch.int32 and ids.dim() == 1 and ids.is_contiguous(),
+             "ids must be a contiguous int32 vector")
+    n, row = ids.shape[0], weight.shape[1]
+    if out is None:
+        out = torch.empty((n, row), dtype=weight.dtype, device=weight.device)
+    _require(out.shape == (n, row) and out.dtype == weight.dtype and out.is_contiguous()
+             and out.device == weight.device, "out must be contiguous [n, row] of weight's dtype")
+    st = lib().pkv_indexing(out.data_ptr(), weight.data_ptr(), weight.shape[0], row,
+                            weight.element_size(), ids.data_ptr(), n, start, _stream(weight))
+    check(st, "pkv_indexing")
+    return out
+
+
 def workspace(B: int, Hq: int, D: int, splits: int, device) -> tuple[torch.Tensor, torch.Tensor]:
     """Partial buffers for :func:`paged_decode_attn`: o ``[B,Hq,S,D]`` fp32, lse ``[B,Hq,S]`` fp32."""
     return (torch.empty((B, Hq, splits, D), dtype=torch.float32, device=device),

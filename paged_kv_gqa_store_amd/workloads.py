@@ -256,6 +256,47 @@ def bulk_fill_rows(inp: Inputs, seed: int | None = None):
     return k_rows, v_rows, slots
 
 
+@dataclass(frozen=True)
+class IndexingConfig:
+    """A vocabulary-parallel embedding lookup: the table is split into ``shards``
+    equal slices of ``vocab / shards`` rows; one rank holds one slice."""
+    name: str
+    vocab: int
+    hidden: int
+    shards: int
+    n: int            # token ids per call
+
+    @property
+    def length(self) -> int:
+        return -(-self.vocab // self.shards)
+
+
+INDEXING = {
+    # Llama-3-8B-shaped table (128256 x 4096, bf16), 8-way vocabulary split
+    "llama3_8b_embed_prefill": IndexingConfig("llama3_8b_embed_prefill", 128256, 4096, 8, 65536),
+    "llama3_8b_embed_decode": IndexingConfig("llama3_8b_embed_decode", 128256, 4096, 8, 32),
+}
+
+
+def make_indexing_inputs(cfg: IndexingConfig, rank: int = 0, seed: int = SEED_BASE + 100):
+    """(slice bf16 bits [length, hidden], ids int32 [n], start) for one rank:
+    the slice holds N(0,1) rows, ids are uniform over the whole vocabulary, so
+    about 1/shards of them fall into this rank's slice."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ids = rng.integers(0, cfg.vocab, cfg.n).astype(np.int32)
+    table_ss = np.random.SeedSequence(seed + 1 + rank)
+    start = rank * cfg.length
+    length = min(cfg.length, cfg.vocab - start)
+    return _normal_bf16(table_ss, (length, cfg.hidden)), ids, start
+
+
+def indexing_bytes(ids, start: int, length: int, row_bytes: int) -> int:
+    """Traffic of one lookup: read the ids and the in-slice rows, write every output row."""
+    ids = np.asarray(ids, np.int64)
+    valid = int(((ids >= start) & (ids < start + length)).sum())
+    return 4 * ids.shape[0] + valid * row_bytes + ids.shape[0] * row_bytes
+
+
 def kv_bytes(seq_lens, Hkv: int, D: int, elem_bytes: int = 2) -> int:
     """K+V bytes one decode step must read: sum_b L_b * 2 * Hkv * D * elem_bytes."""
     return int(np.asarray(seq_lens, np.int64).sum()) * 2 * Hkv * D * elem_bytes
@@ -297,4 +338,5 @@ def sample_rows(cfg: Config, k: int, seed: int = 7) -> np.ndarray:
 
 __all__ = ["Config", "CONFIGS", "Inputs", "make_inputs", "custom_config", "contiguous_layout",
            "bulk_fill_rows", "kv_bytes", "attention_bytes", "store_bytes", "roofline_us",
-           "to_bf16_bits", "bf16_bits_to_f32", "sample_rows"]
+           "to_bf16_bits", "bf16_bits_to_f32", "sample_rows", "IndexingConfig", "INDEXING",
+           "make_indexing_inputs", "indexing_bytes"]

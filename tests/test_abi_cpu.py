@@ -27,7 +27,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(["pkv_kv_store", "pkv_paged_decode_attn", "pkv_decode_merge",
-                                         "pkv_num_splits", "pkv_split_chunk", "pkv_status_str"])
+                                         "pkv_num_splits", "pkv_split_chunk", "pkv_status_str",
+                                         "pkv_indexing"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -87,6 +88,17 @@ def test_store_validation(lib):
     assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, p, -1, 8, 2, None) == SHAPE
     assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, p, 3, 9, 2, None) == SHAPE        # row > stride
     assert lib.pkv_kv_store(p, p, 10, 8, p, p, 8, p, 3, 8, 3, None) == UNSUP
+
+
+def test_indexing_validation(lib):
+    p = ctypes.c_void_p(16)
+    assert lib.pkv_indexing(p, p, 10, 8, 2, p, 0, 0, None) == OK                # n == 0: no launch
+    assert lib.pkv_indexing(None, p, 10, 8, 2, p, 3, 0, None) == NULL
+    assert lib.pkv_indexing(p, None, 10, 8, 2, p, 3, 0, None) == NULL
+    assert lib.pkv_indexing(p, p, 10, 8, 2, None, 3, 0, None) == NULL
+    assert lib.pkv_indexing(p, p, -1, 8, 2, p, 3, 0, None) == SHAPE
+    assert lib.pkv_indexing(p, p, 10, 8, 2, p, -3, 0, None) == SHAPE
+    assert lib.pkv_indexing(p, p, 10, 8, 3, p, 3, 0, None) == UNSUP
 
 
 def _attn(lib, **kw):
