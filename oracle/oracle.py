@@ -83,6 +83,8 @@ def _load(path: Path | None = None):
         lib.oracle_paged_decode_split.restype = ctypes.c_int
         lib.oracle_merge.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p]
         lib.oracle_merge.restype = None
+        lib.oracle_rope.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _i64]
+        lib.oracle_rope.restype = ctypes.c_int
         lib.oracle_indexing.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i64]
         lib.oracle_indexing.restype = None
         lib.oracle_num_threads.argtypes = []
@@ -128,6 +130,29 @@ def kv_store(k_pool, v_pool, k_new, v_new, slot_mapping, row_elems=None):
                                  row_elems * it)
     _check(rc, "kv_store")
     return k_out, v_out
+
+
+def rope(x, positions, cos, sin, heads: int):
+    """Rotary embedding of bf16 rows: ``x`` uint16 ``[n, heads*D]`` (or any
+    shape with ``n`` leading rows of ``heads*D`` elements), ``positions`` int32
+    ``[n]``, ``cos``/``sin`` float32 ``[rows, D/2]``.  Returns uint16 rows of
+    the same shape (see ``oracle_rope`` for the rounding)."""
+    x = _c(x, np.uint16)
+    shape = x.shape
+    n = shape[0]
+    x2 = x.reshape(n, -1)
+    D = x2.shape[1] // heads
+    assert heads * D == x2.shape[1] and D % 2 == 0
+    cos = _c(cos, np.float32)
+    sin = _c(sin, np.float32)
+    assert cos.shape == sin.shape and cos.shape[1] == D // 2
+    pos = _c(positions, np.int32)
+    assert pos.shape == (n,)
+    out = np.empty_like(x2)
+    rc = _load().oracle_rope(_ptr(out), _ptr(x2), n, heads, D, x2.shape[1], _ptr(pos), _ptr(cos),
+                             _ptr(sin), cos.shape[0])
+    _check(rc, "rope")
+    return out.reshape(shape)
 
 
 def indexing(weight, ids, start: int):

@@ -27,6 +27,11 @@
  *   [merge]  cuDNN frontend "CSA Fused Compressor", section "ratio=128": a
  *            chunked softmax keeps a (max, denominator, accumulator) triple
  *            per chunk and merges them in one fixed order.
+ *   [rope]   AstrAI "CUDA Kernels", section "Rotary Embedding Kernel": the
+ *            rotary embedding looks up fp32 cos/sin for the token's position
+ *            and rotates each (head, dimension pair); its reference is a
+ *            complex multiply, i.e. the pair (x[2i], x[2i+1]) is the complex
+ *            number x[2i] + i x[2i+1], multiplied by cos + i sin.
  *   [index]  mini-sglang handbook, "Custom CUDA kernels", section "Moving
  *            whole rows by index": the embedding lookup copies row
  *            ids[t] - start of this rank's vocabulary slice to output row t,
@@ -70,6 +75,47 @@ int oracle_kv_store(uint8_t *k_pool, uint8_t *v_pool, int64_t num_slots,
         if (slot < 0 || slot >= num_slots) return -1;
         memcpy(k_pool + slot * pool_row_stride, k_new + i * in_row_stride, (size_t)row_bytes);
         memcpy(v_pool + slot * pool_row_stride, v_new + i * in_row_stride, (size_t)row_bytes);
+    }
+    return 0;
+}
+
+/* fp32 -> bf16 bits, round to nearest, ties to even; NaN -> quiet NaN 0x7fc0. */
+static uint16_t float_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7fffu + lsb) >> 16);
+}
+
+/* [rope] Rotate rows of n tokens, each `heads` heads of D bf16 elements at
+ * row stride `stride` (elements), by the angle table row positions[t]:
+ *     re = x0*c - x1*s,  im = x0*s + x1*c      (c, s = cos/sin[pos, i])
+ * for every pair (x0, x1) = (x[2i], x[2i+1]).  The rounding is fixed so that
+ * the result is reproducible bit for bit: each product and the sum/difference
+ * is one fp32 operation in this order (no contraction: built with
+ * -ffp-contract=off), then one bf16 round-to-nearest-even.  Output rows are
+ * written contiguously ([n, heads*D]).  Returns 0, or -1 on a position
+ * outside [0, table_rows). */
+int oracle_rope(uint16_t *out, const uint16_t *x, int64_t n, int64_t heads, int64_t D,
+                int64_t stride, const int32_t *positions, const float *cos_t,
+                const float *sin_t, int64_t table_rows) {
+    const int64_t half = D / 2;
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t pos = positions[t];
+        if (pos < 0 || pos >= table_rows) return -1;
+        for (int64_t h = 0; h < heads; ++h) {
+            const uint16_t *xr = x + t * stride + h * D;
+            uint16_t *orow = out + (t * heads + h) * D;
+            for (int64_t i = 0; i < half; ++i) {
+                const float x0 = (float)bf16_to_double(xr[2 * i]);
+                const float x1 = (float)bf16_to_double(xr[2 * i + 1]);
+                const float c = cos_t[pos * half + i], sn = sin_t[pos * half + i];
+                const float a = x0 * c, b = x1 * sn, e = x0 * sn, f = x1 * c;
+                orow[2 * i] = float_to_bf16_rne(a - b);
+                orow[2 * i + 1] = float_to_bf16_rne(e + f);
+            }
+        }
     }
     return 0;
 }

@@ -297,6 +297,17 @@ def indexing_bytes(ids, start: int, length: int, row_bytes: int) -> int:
     return 4 * ids.shape[0] + valid * row_bytes + ids.shape[0] * row_bytes
 
 
+def rope_tables(rows: int, D: int, base: float = 500000.0):
+    """fp32 cos/sin tables ``[rows, D/2]`` of the usual rotary frequencies
+    ``theta_i = base^(-2i/D)`` (Llama-3 uses base 500000): entry (p, i) is the
+    cosine / sine of ``p * theta_i``, evaluated in fp64 and rounded to fp32.
+    These are inputs of the rotary step, like the weights of a model."""
+    i = np.arange(D // 2, dtype=np.float64)
+    theta = base ** (-2.0 * i / D)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def kv_bytes(seq_lens, Hkv: int, D: int, elem_bytes: int = 2) -> int:
     """K+V bytes one decode step must read: sum_b L_b * 2 * Hkv * D * elem_bytes."""
     return int(np.asarray(seq_lens, np.int64).sum()) * 2 * Hkv * D * elem_bytes
@@ -339,4 +350,4 @@ def sample_rows(cfg: Config, k: int, seed: int = 7) -> np.ndarray:
 __all__ = ["Config", "CONFIGS", "Inputs", "make_inputs", "custom_config", "contiguous_layout",
            "bulk_fill_rows", "kv_bytes", "attention_bytes", "store_bytes", "roofline_us",
            "to_bf16_bits", "bf16_bits_to_f32", "sample_rows", "IndexingConfig", "INDEXING",
-           "make_indexing_inputs", "indexing_bytes"]
+           "make_indexing_inputs", "indexing_bytes", "rope_tables"]

@@ -32,6 +32,15 @@ MUTANTS = [
      "if (t1 > seq_lens[b]) t1 = seq_lens[b] - 1;"),
     ("bf16 widened wrongly", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     ("chunk not page aligned", "return (per + page_size - 1) / page_size * page_size;", "return per;"),
+    ("rope real part sign", "orow[2 * i] = float_to_bf16_rne(a - b);", "orow[2 * i] = float_to_bf16_rne(a + b);"),
+    ("rope imaginary part sign", "orow[2 * i + 1] = float_to_bf16_rne(e + f);",
+     "orow[2 * i + 1] = float_to_bf16_rne(f - e);"),
+    ("rope position off by one", "const float c = cos_t[pos * half + i], sn = sin_t[pos * half + i];",
+     "const int64_t pp = pos > 0 ? pos - 1 : 0; const float c = cos_t[pp * half + i], sn = sin_t[pp * half + i];"),
+    ("rope cos and sin swapped", "const float c = cos_t[pos * half + i], sn = sin_t[pos * half + i];",
+     "const float sn = cos_t[pos * half + i], c = sin_t[pos * half + i];"),
+    ("rope pairs halves instead of neighbours", "const float x1 = (float)bf16_to_double(xr[2 * i + 1]);",
+     "const float x1 = (float)bf16_to_double(xr[(2 * i + D / 2) % D]);"),
     ("indexing ignores the slice start", "const int64_t local = (int64_t)ids[t] - start;",
      "const int64_t local = (int64_t)ids[t];"),
     ("indexing leaves masked rows unwritten", "memset(out + t * row_bytes, 0, (size_t)row_bytes);",
@@ -49,6 +58,10 @@ PIN_CALLS = [
     (pins.test_merge_closed_forms, ()),
     (pins.test_split_chunk_reading, ()),
     (pins.test_split_then_merge_equals_unsplit, (3,)),
+    (pins.test_rope_closed_forms, ()),
+    (pins.test_rope_within_one_rounding_of_the_exact_rotation, ()),
+    (pins.test_rope_matches_torch_complex_multiply, ()),
+    (pins.test_rope_preserves_relative_position, ()),
     (pins.test_indexing_matches_torch_embedding, ()),
     (pins.test_indexing_shards_sum_to_the_full_lookup, ()),
     (pins.test_indexing_closed_forms, ()),

@@ -343,3 +343,76 @@ def test_indexing_closed_forms():
     far = np.array([-1, 50, 1 << 30, -(1 << 30)], np.int32)
     assert not oracle.indexing(as_bytes, far, 0).any()
     assert oracle.indexing(as_bytes, np.zeros(0, np.int32), 0).shape == (0, 6)
+
+
+# ----------------------------------------------------------------- rope ----
+# AstrAI "CUDA Kernels", section "Rotary Embedding Kernel": fp32 cos/sin of the
+# token's position rotate each (head, dimension pair); the reference is a
+# complex multiply of the pair (x[2i] + i x[2i+1]) by (cos + i sin).
+
+def _rope_case(n=64, heads=3, D=128, seed=21, rows=4096):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = W.to_bf16_bits(rng.standard_normal((n, heads * D)).astype(np.float32))
+    pos = rng.integers(0, rows, n).astype(np.int32)
+    cos, sin = W.rope_tables(rows, D)
+    return x, pos, cos, sin, heads, D
+
+
+def test_rope_closed_forms():
+    x, _, _, _, heads, D = _rope_case(n=8)
+    half = D // 2
+    ident = (np.ones((1, half), np.float32), np.zeros((1, half), np.float32))
+    quarter = (np.zeros((1, half), np.float32), np.ones((1, half), np.float32))
+    zero = np.zeros(8, np.int32)
+    assert oracle.rope(x, zero, *ident, heads).tobytes() == x.tobytes()
+    got = oracle.rope(x, zero, *quarter, heads).reshape(8, heads, half, 2)
+    xx = x.reshape(8, heads, half, 2)
+    assert (got[..., 0] == (xx[..., 1] ^ np.uint16(0x8000))).all()   # re = -x1 (sign flip of a bf16)
+    assert (got[..., 1] == xx[..., 0]).all()                          # im = x0
+
+
+def test_rope_within_one_rounding_of_the_exact_rotation():
+    x, pos, cos, sin, heads, D = _rope_case()
+    got = _f64(oracle.rope(x, pos, cos, sin, heads)).reshape(len(pos), heads, D // 2, 2)
+    xx = _f64(x).reshape(len(pos), heads, D // 2, 2)
+    c = cos[pos].astype(np.float64)[:, None, :]
+    s = sin[pos].astype(np.float64)[:, None, :]
+    re = xx[..., 0] * c - xx[..., 1] * s
+    im = xx[..., 0] * s + xx[..., 1] * c
+    for g, e in ((got[..., 0], re), (got[..., 1], im)):
+        assert (np.abs(g - e) <= 2.0 ** -8 * np.abs(e) + 1e-30).all()
+
+
+def test_rope_matches_torch_complex_multiply():
+    x, pos, cos, sin, heads, D = _rope_case()
+    got = oracle.rope(x, pos, cos, sin, heads)
+    xt = torch.from_numpy(W.bf16_bits_to_f32(x)).view(len(pos), heads, D // 2, 2)
+    rot = torch.complex(torch.from_numpy(cos[pos]), torch.from_numpy(sin[pos]))[:, None, :]
+    ref = torch.view_as_real(torch.view_as_complex(xt.contiguous()) * rot).reshape(len(pos), heads * D)
+    ref_bits = ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    differ = got != ref_bits
+    # the library's complex product may round its fp32 intermediates differently:
+    # at most one bf16 step apart, and rarely
+    assert differ.mean() < 1e-3
+    assert (np.abs(_f64(got) - _f64(ref_bits)) <= 2.0 ** -7 * np.abs(_f64(ref_bits)) + 1e-30).all()
+
+
+def test_rope_preserves_relative_position():
+    """<rope(q, p), rope(k, t)> depends on p - t only: shifting both positions
+    by the same amount leaves the score unchanged up to bf16 rounding."""
+    rng = np.random.Generator(np.random.PCG64(4))
+    D, rows = 128, 8192
+    cos, sin = W.rope_tables(rows, D)
+    q = W.to_bf16_bits(rng.standard_normal((1, D)).astype(np.float32))
+    k = W.to_bf16_bits(rng.standard_normal((1, D)).astype(np.float32))
+    dots = []
+    for shift in (0, 1000, 5000):
+        rq = _f64(oracle.rope(q, np.array([100 + shift], np.int32), cos, sin, 1))
+        rk = _f64(oracle.rope(k, np.array([37 + shift], np.int32), cos, sin, 1))
+        dots.append(float((rq * rk).sum()))
+    scale = float(np.linalg.norm(_f64(q)) * np.linalg.norm(_f64(k)))
+    assert max(dots) - min(dots) <= 1e-2 * scale
+    # and a different offset gives a different score
+    rq = _f64(oracle.rope(q, np.array([100], np.int32), cos, sin, 1))
+    rk = _f64(oracle.rope(k, np.array([100], np.int32), cos, sin, 1))
+    assert abs(float((rq * rk).sum()) - dots[0]) > 1e-2 * scale
