@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="report the eagerly launched steps instead of one graph replay of K steps")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the secondary measurements (embedding row gather)")
+                    help="skip the secondary measurements (rotary store and attention, embedding row gather)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size reference "
                          "for the HBM byte counters of a profiler run)")
@@ -256,6 +256,35 @@ def main():
     store_gbps = store_b / (bulk_us * 1e-6) / 1e9
     log(f"[bench] kv_store bulk fill: {bslots.shape[0]} rows, {store_b / 1e6:.1f} MB in {bulk_us:.1f} us = "
         f"{store_gbps:.0f} GB/s ({store_gbps / PEAK_HBM_GBPS:.1%})")
+    rope_info = None
+    if not args.no_extras:
+        # the same bulk fill through the store with rotary embedding of K, and the
+        # attention with q rotated in its prologue
+        positions = np.concatenate([np.arange(int(L), dtype=np.int32) for L in inp.seq_lens] +
+                                   [np.zeros(0, np.int32)])
+        c_t, s_t = W.rope_tables(max_len, D)
+        cd, sd = torch.from_numpy(c_t).to(dev), torch.from_numpy(s_t).to(dev)
+        pos_d = to_i32(positions)
+        k3, v3 = k_rows_d.view(-1, Hkv, D), v_rows_d.view(-1, Hkv, D)
+        us = time_launches(lambda i: pkv.kv_store_rope(pools[i % len(pools)][0], pools[i % len(pools)][1],
+                                                       k3, v3, bslots_d, pos_d, cd, sd), reps=args.store_reps)
+        rope_b = store_b + 4 * bslots.shape[0] + max_len * D * 4   # + positions, cos/sin tables once
+        qpos = to_i32(np.maximum(inp.seq_lens - 1, 0))
+        ua = time_launches(lambda i: pkv.paged_decode_attn(
+            q, pools[i % len(pools)][0], pools[i % len(pools)][1], page_table, seq_lens, max_len, S,
+            o_partial=o_p, lse_partial=l_p, q_positions=qpos, rope_cos=cd, rope_sin=sd), reps=30)
+        ub = time_launches(lambda i: pkv.paged_decode_attn(
+            q, pools[i % len(pools)][0], pools[i % len(pools)][1], page_table, seq_lens, max_len, S,
+            o_partial=o_p, lse_partial=l_p), reps=30)
+        rope_info = {
+            "kv_store_rope_bulk_us": round(us, 2),
+            "kv_store_rope_bulk_GBps": round(rope_b / (us * 1e-6) / 1e9, 1),
+            "kv_store_rope_bulk_pct_of_peak": round(100 * rope_b / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+            "attn_rope_us": round(ua, 2), "attn_plain_us_same_loop": round(ub, 2),
+        }
+        log(f"[bench] kv_store_rope bulk fill: {us:.1f} us = {rope_b / (us * 1e-6) / 1e9:.0f} GB/s; "
+            f"attention with q rotated in the prologue {ua:.1f} us vs {ub:.1f} us plain (back to back)")
+        del cd, sd, pos_d
     del k_rows_d, v_rows_d, bslots_d
 
     result = {
@@ -302,6 +331,7 @@ def main():
     }
 
     if not args.no_extras:
+        result["rope"] = rope_info
         result["extras"] = measure_extras(args, pkv, W, dev, to_bf16, to_i32)
 
     if args.copy_calibration:

@@ -3,6 +3,8 @@
  * over a paged KV cache, on AMD MI355X (gfx950).
  *
  *   pkv_kv_store          scatter the step's new K/V rows into the page pool
+ *   pkv_kv_store_rope     the store with K rows rotated by a rotary embedding on the way
+ *   pkv_paged_decode_attn_rope  the attention with q rotated in its prologue
  *   pkv_indexing          row gather from a vocabulary slice (embedding lookup)
  *   pkv_paged_decode_attn split-KV attention through the page table -> partials
  *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
@@ -75,6 +77,61 @@ pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t p
                         const void *k_new, const void *v_new, int64_t in_row_stride,
                         const int32_t *slot_mapping, int64_t n, int64_t row_elems,
                         int32_t elem_bytes, void *stream);
+
+/*
+ * Rotary embedding (both entry points below).
+ *
+ * Follows: AstrAI "CUDA Kernels", section "Rotary Embedding Kernel" (fp32
+ * cos/sin of a token's position rotate every (head, dimension pair); the
+ * reference is a complex multiply).  Rows are bf16; within each head of D
+ * elements the pair (x[2i], x[2i+1]) is the complex number x[2i] + i x[2i+1],
+ * multiplied by cos[pos, i] + i sin[pos, i]:
+ *     x'[2i]   = x[2i] * c - x[2i+1] * s
+ *     x'[2i+1] = x[2i] * s + x[2i+1] * c
+ * each product and the difference/sum one fp32 operation in this order (no
+ * fused multiply-add), then one bf16 round-to-nearest-even per element (NaN ->
+ * 0x7fc0).  Tables: rope_cos, rope_sin fp32 [rope_rows, D/2], contiguous,
+ * 16-byte aligned (else PKV_ERR_ALIGN); the caller fills them (for example
+ * with theta_i = base^(-2i/D) and angle = pos * theta_i).  A position outside
+ * [0, rope_rows) rotates nothing: the affected row comes out NaN.
+ */
+
+/*
+ * pkv_kv_store_rope -- pkv_kv_store for bf16 rows of Hkv heads x D, with every
+ * K row rotated by the rotary embedding of positions[i] before it is written
+ * (V rows are copied unchanged).  The rotated K goes straight to the pool: no
+ * separate pass over K.
+ *   positions  device int32 [n]: position of new row i (its table row)
+ *   Hkv, D     heads per row and head size (D a multiple of 8); rows are
+ *              Hkv*D bf16 elements, strides in elements
+ * Both pool and input bases and strides must be 16-byte multiples (else
+ * PKV_ERR_ALIGN).  Slots as for pkv_kv_store (outside the pool: skipped).
+ * Returns PKV_OK (n == 0: nothing launched), PKV_ERR_NULL, PKV_ERR_SHAPE,
+ * PKV_ERR_ALIGN, PKV_ERR_HIP.
+ */
+pkv_status pkv_kv_store_rope(void *k_pool, void *v_pool, int64_t num_slots,
+                             int64_t pool_row_stride, const void *k_new, const void *v_new,
+                             int64_t in_row_stride, const int32_t *slot_mapping, int64_t n,
+                             int32_t Hkv, int32_t D, const int32_t *positions,
+                             const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                             void *stream);
+
+/*
+ * pkv_paged_decode_attn_rope -- pkv_paged_decode_attn with q rotated by the
+ * rotary embedding of q_positions[b] (device int32 [B]) in the kernel's
+ * prologue; the rotated q is rounded to bf16 exactly as a separately rotated
+ * q would be, so the result equals pkv_paged_decode_attn on that q, bit for
+ * bit.  Other arguments, layouts and status codes as pkv_paged_decode_attn.
+ */
+pkv_status pkv_paged_decode_attn_rope(const void *q, const void *k_pool, const void *v_pool,
+                                      const int32_t *page_table, const int32_t *seq_lens,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t page_size, int32_t num_pages,
+                                      int32_t max_pages_per_seq, int32_t max_seq_len,
+                                      int32_t num_splits, float scale, float *o_partial,
+                                      float *lse_partial, const int32_t *q_positions,
+                                      const float *rope_cos, const float *rope_sin,
+                                      int32_t rope_rows, void *stream);
 
 /*
  * pkv_indexing -- row gather from one rank's slice of a vocabulary-parallel

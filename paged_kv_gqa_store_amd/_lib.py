@@ -19,6 +19,10 @@ _f32 = ctypes.c_float
 SIGNATURES = [
     ("pkv_kv_store", _i32, [_p, _p, _i64, _i64, _p, _p, _i64, _p, _i64, _i64, _i32, _p]),
     ("pkv_indexing", _i32, [_p, _p, _i64, _i64, _i32, _p, _i64, _i64, _p]),
+    ("pkv_kv_store_rope", _i32, [_p, _p, _i64, _i64, _p, _p, _i64, _p, _i64, _i32, _i32, _p, _p, _p,
+                                 _i32, _p]),
+    ("pkv_paged_decode_attn_rope", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _f32, _p, _p, _p, _p, _p, _i32, _p]),
     ("pkv_paged_decode_attn", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _f32, _p, _p, _p]),
     ("pkv_decode_merge", _i32, [_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),

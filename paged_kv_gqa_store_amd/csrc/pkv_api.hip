@@ -32,6 +32,63 @@ int copy_unit(std::initializer_list<uint64_t> vals) {
 
 constexpr int kMaxSplits = 1024;
 
+
+// Validates the arguments shared by both attention entry points and fills the
+// launch parameters; PKV_OK with p.B == 0 means "nothing to launch".
+pkv_status attention_params(const void *q, const void *k_pool, const void *v_pool,
+                            const int32_t *page_table, const int32_t *seq_lens, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                            int32_t num_pages, int32_t max_pages_per_seq, int32_t max_seq_len,
+                            int32_t num_splits, float scale, float *o_partial,
+                            float *lse_partial, pkv::DecodeParams &p) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_seq_len < 0 ||
+      num_splits < 1 || num_splits > kMaxSplits)
+    return PKV_ERR_SHAPE;
+  if (Hq % Hkv) return PKV_ERR_SHAPE;
+  const int G = Hq / Hkv;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size > 1024) return PKV_ERR_UNSUPPORTED;
+  if (int64_t(max_seq_len) > int64_t(max_pages_per_seq) * page_size) return PKV_ERR_SHAPE;
+  if (B > 65535 || Hkv > 65535) return PKV_ERR_SHAPE;
+  if (int64_t(num_splits) * Hkv * B > int64_t(INT32_MAX)) return PKV_ERR_SHAPE;   // grid size
+  if (int64_t(num_pages) * page_size > (int64_t(1) << 31)) return PKV_ERR_SHAPE;
+  if (int64_t(max_pages_per_seq) * page_size > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return PKV_ERR_SHAPE;
+  p = pkv::DecodeParams{};
+  p.B = B;
+  if (B == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o_partial || !lse_partial)
+    return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_ALIGN;
+  p.q = static_cast<const uint16_t *>(q);
+  p.k_pool = static_cast<const uint16_t *>(k_pool);
+  p.v_pool = static_cast<const uint16_t *>(v_pool);
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.o_partial = o_partial;
+  p.lse_partial = lse_partial;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.G = G;
+  p.page_log2 = log2_exact(page_size);
+  p.num_pages = num_pages;
+  p.max_pages = max_pages_per_seq;
+  p.num_splits = num_splits;
+  p.chunk = max_seq_len == 0 ? page_size : pkv_split_chunk(max_seq_len, num_splits, page_size);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return PKV_OK;
+}
+
+// fp32 cos/sin tables of rope_rows rows of D/2 values, 16-byte aligned
+pkv_status rope_table_check(const float *rope_cos, const float *rope_sin, int32_t rope_rows) {
+  if (rope_rows < 1) return PKV_ERR_SHAPE;
+  if (!rope_cos || !rope_sin) return PKV_ERR_NULL;
+  if (!aligned16(rope_cos) || !aligned16(rope_sin)) return PKV_ERR_ALIGN;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,6 +155,31 @@ pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t p
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+pkv_status pkv_kv_store_rope(void *k_pool, void *v_pool, int64_t num_slots,
+                             int64_t pool_row_stride, const void *k_new, const void *v_new,
+                             int64_t in_row_stride, const int32_t *slot_mapping, int64_t n,
+                             int32_t Hkv, int32_t D, const int32_t *positions,
+                             const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                             void *stream) {
+  if (n < 0 || num_slots < 0 || Hkv < 1 || D < 8 || D % 8) return PKV_ERR_SHAPE;
+  const int64_t row_elems = int64_t(Hkv) * D;
+  if (row_elems > pool_row_stride || row_elems > in_row_stride) return PKV_ERR_SHAPE;
+  if (num_slots > (int64_t(1) << 31) || n > (int64_t(1) << 40)) return PKV_ERR_SHAPE;
+  const pkv_status st = rope_table_check(rope_cos, rope_sin, rope_rows);
+  if (st != PKV_OK) return st;
+  if (n == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping || !positions) return PKV_ERR_NULL;
+  if (copy_unit({uint64_t(pool_row_stride * 2), uint64_t(in_row_stride * 2),
+                 reinterpret_cast<uintptr_t>(k_pool), reinterpret_cast<uintptr_t>(v_pool),
+                 reinterpret_cast<uintptr_t>(k_new), reinterpret_cast<uintptr_t>(v_new)}) != 16)
+    return PKV_ERR_ALIGN;
+  hipError_t e = pkv::launch_kv_store_rope(k_pool, v_pool, num_slots, pool_row_stride * 2, k_new,
+                                           v_new, in_row_stride * 2, slot_mapping, n, Hkv, D,
+                                           positions, rope_cos, rope_sin, rope_rows,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 pkv_status pkv_indexing(void *out, const void *weight, int64_t length, int64_t row_elems,
                         int32_t elem_bytes, const int32_t *ids, int64_t n, int64_t start,
                         void *stream) {
@@ -115,50 +197,44 @@ pkv_status pkv_indexing(void *out, const void *weight, int64_t length, int64_t r
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+
 pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *v_pool,
                                  const int32_t *page_table, const int32_t *seq_lens, int32_t B,
                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
                                  int32_t num_pages, int32_t max_pages_per_seq,
                                  int32_t max_seq_len, int32_t num_splits, float scale,
                                  float *o_partial, float *lse_partial, void *stream) {
-  if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_seq_len < 0 ||
-      num_splits < 1 || num_splits > kMaxSplits)
-    return PKV_ERR_SHAPE;
-  if (Hq % Hkv) return PKV_ERR_SHAPE;
-  const int G = Hq / Hkv;
-  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
-  if (!is_pow2(page_size) || page_size > 1024) return PKV_ERR_UNSUPPORTED;
-  if (int64_t(max_seq_len) > int64_t(max_pages_per_seq) * page_size) return PKV_ERR_SHAPE;
-  if (B > 65535 || Hkv > 65535) return PKV_ERR_SHAPE;
-  if (int64_t(num_splits) * Hkv * B > int64_t(INT32_MAX)) return PKV_ERR_SHAPE;   // grid size
-  if (int64_t(num_pages) * page_size > (int64_t(1) << 31)) return PKV_ERR_SHAPE;
-  if (int64_t(max_pages_per_seq) * page_size > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
-  if (!(scale > 0.f) || !isfinite(scale)) return PKV_ERR_SHAPE;
-  if (B == 0) return PKV_OK;
-  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o_partial || !lse_partial)
-    return PKV_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_ALIGN;
-
   pkv::DecodeParams p;
-  p.q = static_cast<const uint16_t *>(q);
-  p.k_pool = static_cast<const uint16_t *>(k_pool);
-  p.v_pool = static_cast<const uint16_t *>(v_pool);
-  p.page_table = page_table;
-  p.seq_lens = seq_lens;
-  p.o_partial = o_partial;
-  p.lse_partial = lse_partial;
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.D = D;
-  p.G = G;
-  p.page_log2 = log2_exact(page_size);
-  p.num_pages = num_pages;
-  p.max_pages = max_pages_per_seq;
-  p.num_splits = num_splits;
-  p.chunk = max_seq_len == 0 ? page_size : pkv_split_chunk(max_seq_len, num_splits, page_size);
-  p.scale_log2 = scale * 1.4426950408889634f;
+  const pkv_status st = attention_params(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D,
+                                         page_size, num_pages, max_pages_per_seq, max_seq_len,
+                                         num_splits, scale, o_partial, lse_partial, p);
+  if (st != PKV_OK || p.B == 0) return st;
+  hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_paged_decode_attn_rope(const void *q, const void *k_pool, const void *v_pool,
+                                      const int32_t *page_table, const int32_t *seq_lens,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t page_size, int32_t num_pages,
+                                      int32_t max_pages_per_seq, int32_t max_seq_len,
+                                      int32_t num_splits, float scale, float *o_partial,
+                                      float *lse_partial, const int32_t *q_positions,
+                                      const float *rope_cos, const float *rope_sin,
+                                      int32_t rope_rows, void *stream) {
+  pkv::DecodeParams p;
+  pkv_status st = attention_params(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D,
+                                   page_size, num_pages, max_pages_per_seq, max_seq_len,
+                                   num_splits, scale, o_partial, lse_partial, p);
+  if (st != PKV_OK) return st;
+  st = rope_table_check(rope_cos, rope_sin, rope_rows);
+  if (st != PKV_OK) return st;
+  if (p.B == 0) return PKV_OK;
+  if (!q_positions) return PKV_ERR_NULL;
+  p.q_pos = q_positions;
+  p.rope_cos = rope_cos;
+  p.rope_sin = rope_sin;
+  p.rope_rows = rope_rows;
   hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

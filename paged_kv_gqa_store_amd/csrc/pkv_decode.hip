@@ -147,10 +147,17 @@ __global__ __launch_bounds__(256) void paged_decode_valu_kernel(DecodeParams p) 
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
+    bool nan = false;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 0; w < kWaves; ++w) {
+      M = fmaxf(M, sm_m[w][h]);
+      nan |= sm_l[w][h] != sm_l[w][h];
+    }
     const size_t orow = (size_t(b) * p.Hq + size_t(g) * G + h) * p.num_splits + s;
-    if (M == -INFINITY) {
+    // Empty split: no position seen.  A split whose every score was NaN also
+    // leaves the running max at -inf (fmaxf drops NaN) but its sum is NaN, and
+    // it must come out NaN, so it takes the general path (NaN * 0 stays NaN).
+    if (M == -INFINITY && !nan) {
       p.o_partial[orow * D + d] = 0.f;
       if (d == 0) p.lse_partial[orow] = -INFINITY;
       continue;
@@ -226,7 +233,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restri
 
 hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
   const char *v = getenv("PKV_DECODE_KERNEL");
-  if (v && strcmp(v, "valu") == 0) return launch_paged_decode_valu(p, stream);
+  // the VALU kernel has no rotary-embedding prologue; rotated-q calls always
+  // take the matrix-core kernel
+  if (v && strcmp(v, "valu") == 0 && !p.q_pos) return launch_paged_decode_valu(p, stream);
   return launch_paged_decode_mfma(p, stream);
 }
 

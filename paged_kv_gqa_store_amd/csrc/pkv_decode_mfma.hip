@@ -93,7 +93,7 @@ __device__ __forceinline__ void pin_issue_order() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int G, bool kPageTile, int NBUF, int kWaves>
+template <int D, int G, bool kPageTile, int NBUF, int kWaves, bool kRope>
 __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodeParams p) {
   constexpr int KS = D / 32;      // MFMA k-steps per tile = V loads per lane per tile
   constexpr int LPV = D / 8;      // lanes per token in the V layout
@@ -137,10 +137,29 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   // q rows of the group as the MFMA A operand: lane = head (lane & 15), dims 32j + 8(lane >> 4)
   const int qh = lane & 15, qk = lane >> 4;
   bf16x8 qa[KS];
+  [[maybe_unused]] const float *rc = nullptr, *rs = nullptr;
+  [[maybe_unused]] bool pos_ok = true;
+  if constexpr (kRope) {
+    // rotary embedding of q (AstrAI "CUDA Kernels", section "Rotary Embedding
+    // Kernel"): a lane's 8 dims are 4 whole pairs, rotated by the cos/sin row of
+    // this sequence's query position and rounded to bf16 like the stored K.
+    const int pos = p.q_pos[b];
+    pos_ok = pos >= 0 && pos < p.rope_rows;
+    rc = p.rope_cos + size_t(pos_ok ? pos : 0) * (D / 2);
+    rs = p.rope_sin + size_t(pos_ok ? pos : 0) * (D / 2);
+  }
 #pragma unroll
   for (int j = 0; j < KS; ++j) {
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (qh < G) w = ld16(p.q + (size_t(b) * p.Hq + size_t(g) * G + qh) * D + 32 * j + 8 * qk);
+    if (qh < G) {
+      w = ld16(p.q + (size_t(b) * p.Hq + size_t(g) * G + qh) * D + 32 * j + 8 * qk);
+      if constexpr (kRope) {
+        const f32x4 c = *reinterpret_cast<const f32x4 *>(rc + 16 * j + 4 * qk);
+        const f32x4 sn = *reinterpret_cast<const f32x4 *>(rs + 16 * j + 4 * qk);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = pos_ok ? rope_pair(w[k], c[k], sn[k]) : 0x7fc07fc0u;
+      }
+    }
     qa[j] = as_bf16x8(w);
   }
   // Make q resident now: otherwise the first use inside the pipelined loop
@@ -344,10 +363,17 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
+    bool nan = false;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 0; w < kWaves; ++w) {
+      M = fmaxf(M, sm_m[w][h]);
+      nan |= sm_l[w][h] != sm_l[w][h];
+    }
     const size_t orow = (size_t(b) * p.Hq + size_t(g) * G + h) * p.num_splits + s;
-    if (M == -INFINITY) {
+    // Empty split: no position seen.  A split whose every score was NaN also
+    // leaves the running max at -inf (fmaxf drops NaN) but its sum is NaN, and
+    // it must come out NaN, so it takes the general path (NaN * 0 stays NaN).
+    if (M == -INFINITY && !nan) {
       p.o_partial[orow * D + d] = 0.f;
       if (d == 0) p.lse_partial[orow] = -INFINITY;
       continue;
@@ -365,23 +391,26 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool kRope>
 hipError_t launch_mfma(const DecodeParams &p, hipStream_t stream) {
   constexpr int kWaves = 4;
   const dim3 grid{unsigned(p.num_splits * p.Hkv * p.B)}, block{kWaves * 64};
   constexpr int NBUF = D == 128 ? 3 : 4;
   if (p.page_log2 >= 4)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, kWaves>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, kWaves, kRope>), grid, block, 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false, NBUF, kWaves>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false, NBUF, kWaves, kRope>), grid, block, 0,
+                       stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_paged_decode_mfma(const DecodeParams &p, hipStream_t stream) {
-#define PKV_CASE(DD, GG) \
-  if (p.D == DD && p.G == GG) return launch_mfma<DD, GG>(p, stream);
+#define PKV_CASE(DD, GG)                                                        \
+  if (p.D == DD && p.G == GG)                                                   \
+    return p.q_pos ? launch_mfma<DD, GG, true>(p, stream) : launch_mfma<DD, GG, false>(p, stream);
   PKV_CASE(64, 1) PKV_CASE(64, 2) PKV_CASE(64, 4) PKV_CASE(64, 8)
   PKV_CASE(128, 1) PKV_CASE(128, 2) PKV_CASE(128, 4) PKV_CASE(128, 8)
 #undef PKV_CASE

@@ -27,6 +27,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Rotary embedding of one 32-bit word holding the pair (x[2i], x[2i+1]) of
+// bf16 values (x[2i] in the low half): the pair is the complex number
+// x[2i] + i x[2i+1], multiplied by c + i s.  Each product and the
+// sum/difference is one fp32 operation (contraction off, so the bits do not
+// depend on FMA formation), then each half rounds once to bf16 (RNE).
+__device__ __forceinline__ uint32_t rope_pair(uint32_t w, float c, float s) {
+#pragma clang fp contract(off)
+  const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+  const float a = x0 * c, b = x1 * s, e = x0 * s, f = x1 * c;
+  return f32_to_bf16_rne(a - b) | (f32_to_bf16_rne(e + f) << 16);
+}
+
 // 2^x on the hardware transcendental unit (v_exp_f32): 2^-inf = 0, 2^0 = 1.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

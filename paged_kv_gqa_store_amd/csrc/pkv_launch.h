@@ -21,12 +21,23 @@ struct DecodeParams {
   int num_pages, max_pages;
   int num_splits, chunk;     // split s covers [s*chunk, (s+1)*chunk)
   float scale_log2;          // softmax scale * log2(e)
+  // rotary embedding of q (all NULL / 0 when q is used as given)
+  const int32_t *q_pos;      // [B] position of each sequence's query token
+  const float *rope_cos;     // [rope_rows, D/2] fp32
+  const float *rope_sin;
+  int rope_rows;
 };
 
 hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,
                            const void *k_new, const void *v_new, int64_t in_stride_b,
                            const int32_t *slots, int64_t n, int64_t row_b, int unit_b,
                            hipStream_t stream);
+
+hipError_t launch_kv_store_rope(void *k_pool, void *v_pool, int64_t num_slots,
+                               int64_t pool_stride_b, const void *k_new, const void *v_new,
+                               int64_t in_stride_b, const int32_t *slots, int64_t n, int Hkv,
+                               int D, const int32_t *positions, const float *rope_cos,
+                               const float *rope_sin, int rope_rows, hipStream_t stream);
 
 hipError_t launch_gather_rows(void *out, const void *weight, int64_t length, const int32_t *ids,
                               int64_t n, int64_t start, int64_t row_b, int unit_b,

@@ -62,6 +62,49 @@ __global__ __launch_bounds__(256) void store_rows_kernel(
   }
 }
 
+// kv_store with rotary embedding (AstrAI "CUDA Kernels", section "Rotary
+// Embedding Kernel": fp32 cos/sin of the token's position rotate every
+// (head, dimension pair)).  K rows are rotated while they are scattered, so the
+// rotated K never makes a separate round trip through memory; V rows are
+// copied as by store_rows_kernel.  bf16 rows of heads*D elements moved in
+// 16-byte units (4 pairs); a unit's pairs need 4 cos and 4 sin values, read
+// as one 16-byte vector each (the table row is shared by the token's heads and
+// stays in cache).  A position outside the table writes a NaN K row.
+__global__ __launch_bounds__(256) void store_rope_kernel(
+    u32x4 *__restrict__ k_pool, u32x4 *__restrict__ v_pool, int64_t num_slots, int64_t pool_stride,
+    const u32x4 *__restrict__ k_new, const u32x4 *__restrict__ v_new, int64_t in_stride,
+    const int32_t *__restrict__ slots, const int32_t *__restrict__ positions,
+    const float *__restrict__ rope_cos, const float *__restrict__ rope_sin, int rope_rows,
+    int64_t n, int64_t row_units, int d_units, int lanes_log2) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int64_t lanes = int64_t(1) << lanes_log2;
+  const int64_t rows_per_grid = (int64_t(gridDim.x) * blockDim.x) >> lanes_log2;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t lane = gid & (lanes - 1);
+  const int half = d_units * 4;                 // D / 2 pairs per head
+  for (int64_t r = gid >> lanes_log2; r < n; r += rows_per_grid) {
+    const int64_t slot = __builtin_nontemporal_load(slots + r);
+    const int pos = __builtin_nontemporal_load(positions + r);
+    const bool pos_ok = pos >= 0 && pos < rope_rows;
+    const float *cr = rope_cos + int64_t(pos_ok ? pos : 0) * half;
+    const float *sr = rope_sin + int64_t(pos_ok ? pos : 0) * half;
+    const u32x4 *ks = k_new + r * in_stride;
+    const u32x4 *vs = v_new + r * in_stride;
+    for (int64_t i = lane; i < row_units; i += lanes) {
+      u32x4 kb = __builtin_nontemporal_load(ks + i);
+      const u32x4 vb = __builtin_nontemporal_load(vs + i);
+      const int p4 = 4 * int(i % d_units);      // first pair of this unit within its head
+      const f32x4 c = *reinterpret_cast<const f32x4 *>(cr + p4);
+      const f32x4 sn = *reinterpret_cast<const f32x4 *>(sr + p4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kb[k] = pos_ok ? rope_pair(kb[k], c[k], sn[k]) : 0x7fc07fc0u;
+      if (slot < 0 || slot >= num_slots) continue;
+      __builtin_nontemporal_store(kb, k_pool + slot * pool_stride + i);
+      __builtin_nontemporal_store(vb, v_pool + slot * pool_stride + i);
+    }
+  }
+}
+
 // indexing: vocabulary-slice row gather (mini-sglang handbook, "Custom CUDA
 // kernels", section "Moving whole rows by index").  Output row r is row
 // ids[r] - start of the slice, or zeros when the id lies outside
@@ -171,6 +214,21 @@ hipError_t launch_gather_rows(void *out, const void *weight, int64_t length, con
     case 2: return launch_gather<uint16_t>(out, weight, length, ids, n, start, row_b, stream);
     default: return launch_gather<uint8_t>(out, weight, length, ids, n, start, row_b, stream);
   }
+}
+
+hipError_t launch_kv_store_rope(void *k_pool, void *v_pool, int64_t num_slots,
+                               int64_t pool_stride_b, const void *k_new, const void *v_new,
+                               int64_t in_stride_b, const int32_t *slots, int64_t n, int Hkv,
+                               int D, const int32_t *positions, const float *rope_cos,
+                               const float *rope_sin, int rope_rows, hipStream_t stream) {
+  const int64_t row_units = int64_t(Hkv) * D / 8;
+  const RowLaunch L = plan_rows(n, row_units);
+  hipLaunchKernelGGL(store_rope_kernel, L.grid, dim3{256}, 0, stream,
+                     static_cast<u32x4 *>(k_pool), static_cast<u32x4 *>(v_pool), num_slots,
+                     pool_stride_b / 16, static_cast<const u32x4 *>(k_new),
+                     static_cast<const u32x4 *>(v_new), in_stride_b / 16, slots, positions,
+                     rope_cos, rope_sin, rope_rows, n, row_units, D / 8, L.lanes_log2);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,

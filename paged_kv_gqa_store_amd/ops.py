@@ -115,6 +115,42 @@ def indexing(weight: torch.Tensor, ids: torch.Tensor, start: int = 0, out=None) 
     return out
 
 
+def _rope_tables(cos: torch.Tensor, sin: torch.Tensor, D: int, dev):
+    _require(cos.dtype == torch.float32 and sin.dtype == torch.float32 and cos.is_contiguous()
+             and sin.is_contiguous() and cos.shape == sin.shape and cos.dim() == 2
+             and cos.shape[1] == D // 2, "rope tables must be contiguous fp32 [rows, D/2]")
+    _require(cos.device == dev and sin.device == dev, "rope tables must be on the GPU of the data")
+
+
+def kv_store_rope(k_pool, v_pool, k_new, v_new, slot_mapping, positions, rope_cos, rope_sin) -> None:
+    """:func:`kv_store` of bf16 rows with every K row rotated by the rotary
+    embedding of ``positions[i]`` on its way into the pool (V copied as is).
+
+    Pools ``[num_pages, page_size, Hkv, D]``; new rows ``[n, Hkv, D]``;
+    ``positions`` int32 ``[n]``; ``rope_cos``/``rope_sin`` fp32 ``[rows, D/2]``."""
+    _on_gpu(k_pool, v_pool, k_new, v_new, slot_mapping, positions)
+    _require(k_pool.dim() == 4 and k_new.dim() == 3, "pools [num_pages,P,Hkv,D], rows [n,Hkv,D]")
+    _require(k_pool.dtype == v_pool.dtype == k_new.dtype == v_new.dtype == torch.bfloat16,
+             "pools and rows must be bfloat16")
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.dim() == 1 and slot_mapping.is_contiguous(),
+             "slot_mapping must be a contiguous int32 vector")
+    _require(positions.dtype == torch.int32 and positions.shape == slot_mapping.shape
+             and positions.is_contiguous(), "positions must be contiguous int32 [n]")
+    Hkv, D = k_pool.shape[2], k_pool.shape[3]
+    _require(k_new.shape[1:] == (Hkv, D) and v_new.shape == k_new.shape, "rows must be [n, Hkv, D]")
+    _rope_tables(rope_cos, rope_sin, D, k_pool.device)
+    kp, vp = _rows(k_pool, "k_pool", True), _rows(v_pool, "v_pool", True)
+    kn, vn = _rows(k_new, "k_new", False), _rows(v_new, "v_new", False)
+    _require(kp.stride() == vp.stride() and kn.stride() == vn.stride(), "k and v must share strides")
+    n = slot_mapping.shape[0]
+    _require(kn.shape[0] == n, "one slot per new row")
+    st = lib().pkv_kv_store_rope(kp.data_ptr(), vp.data_ptr(), kp.shape[0], kp.stride(0), kn.data_ptr(),
+                                 vn.data_ptr(), kn.stride(0), slot_mapping.data_ptr(), n, Hkv, D,
+                                 positions.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(),
+                                 rope_cos.shape[0], _stream(kp))
+    check(st, "pkv_kv_store_rope")
+
+
 def workspace(B: int, Hq: int, D: int, splits: int, device) -> tuple[torch.Tensor, torch.Tensor]:
     """Partial buffers for :func:`paged_decode_attn`: o ``[B,Hq,S,D]`` fp32, lse ``[B,Hq,S]`` fp32."""
     return (torch.empty((B, Hq, splits, D), dtype=torch.float32, device=device),
@@ -123,13 +159,17 @@ def workspace(B: int, Hq: int, D: int, splits: int, device) -> tuple[torch.Tenso
 
 def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
                       splits: int | None = None, scale: float | None = None,
-                      o_partial=None, lse_partial=None, total_tokens: int = -1):
+                      o_partial=None, lse_partial=None, total_tokens: int = -1,
+                      q_positions=None, rope_cos=None, rope_sin=None):
     """Split-KV attention over the paged pool; returns (o_partial, lse_partial).
 
     q ``[B,Hq,D]`` bf16; pools ``[num_pages,P,Hkv,D]`` bf16; page_table int32
     ``[B,max_pages]``; seq_lens int32 ``[B]``; ``max_seq_len`` is a host bound
     on ``seq_lens`` (no device read); ``total_tokens`` (sum of ``seq_lens``, if
-    the caller knows it) only steers the split heuristic when ``splits`` is None."""
+    the caller knows it) only steers the split heuristic when ``splits`` is None.
+    With ``q_positions`` (int32 ``[B]``) and fp32 ``rope_cos``/``rope_sin``
+    ``[rows, D/2]``, q is rotated by the rotary embedding in the kernel's
+    prologue (``pkv_paged_decode_attn_rope``)."""
     _on_gpu(q, k_pool, v_pool, page_table, seq_lens)
     _require(q.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
              "q and the pools must be bfloat16")
@@ -150,11 +190,21 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
     _require(lse_partial.shape == (B, Hq, S) and lse_partial.dtype == torch.float32 and lse_partial.is_contiguous(),
              "lse_partial must be contiguous fp32 [B,Hq,S]")
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    st = lib().pkv_paged_decode_attn(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                                     page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, P,
-                                     num_pages, page_table.shape[1], max_seq_len, S, scale,
-                                     o_partial.data_ptr(), lse_partial.data_ptr(), _stream(q))
-    check(st, "pkv_paged_decode_attn")
+    args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
+            seq_lens.data_ptr(), B, Hq, Hkv, D, P, num_pages, page_table.shape[1], max_seq_len, S,
+            scale, o_partial.data_ptr(), lse_partial.data_ptr())
+    if q_positions is None:
+        st = lib().pkv_paged_decode_attn(*args, _stream(q))
+        check(st, "pkv_paged_decode_attn")
+    else:
+        _on_gpu(q, q_positions)
+        _require(q_positions.dtype == torch.int32 and q_positions.shape == (B,)
+                 and q_positions.is_contiguous(), "q_positions must be contiguous int32 [B]")
+        _require(rope_cos is not None and rope_sin is not None, "q_positions needs rope_cos and rope_sin")
+        _rope_tables(rope_cos, rope_sin, D, q.device)
+        st = lib().pkv_paged_decode_attn_rope(*args, q_positions.data_ptr(), rope_cos.data_ptr(),
+                                              rope_sin.data_ptr(), rope_cos.shape[0], _stream(q))
+        check(st, "pkv_paged_decode_attn_rope")
     return o_partial, lse_partial
 
 

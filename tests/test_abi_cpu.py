@@ -28,7 +28,8 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(["pkv_kv_store", "pkv_paged_decode_attn", "pkv_decode_merge",
                                          "pkv_num_splits", "pkv_split_chunk", "pkv_status_str",
-                                         "pkv_indexing"])
+                                         "pkv_indexing", "pkv_kv_store_rope",
+                                         "pkv_paged_decode_attn_rope"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -99,6 +100,22 @@ def test_indexing_validation(lib):
     assert lib.pkv_indexing(p, p, -1, 8, 2, p, 3, 0, None) == SHAPE
     assert lib.pkv_indexing(p, p, 10, 8, 2, p, -3, 0, None) == SHAPE
     assert lib.pkv_indexing(p, p, 10, 8, 3, p, 3, 0, None) == UNSUP
+
+
+def test_rope_validation(lib):
+    p, f = ctypes.c_void_p(256), ctypes.c_void_p(512)
+    # pools/rows of 1 head x 64, 16-byte aligned; tables of 10 rows
+    ok = lambda **kw: lib.pkv_kv_store_rope(*[kw.get(k, d) for k, d in [
+        ("kp", p), ("vp", p), ("slots_n", 100), ("ps", 64), ("kn", p), ("vn", p), ("is_", 64),
+        ("sm", p), ("n", 3), ("Hkv", 1), ("D", 64), ("pos", p), ("c", f), ("s", f), ("rows", 10)]], None)
+    assert ok(n=0) == OK
+    assert ok(pos=None) == NULL
+    assert ok(c=None) == NULL
+    assert ok(rows=0) == SHAPE
+    assert ok(D=60) == SHAPE
+    assert ok(c=ctypes.c_void_p(516)) == ALIGN
+    assert ok(kp=ctypes.c_void_p(258)) == ALIGN
+    assert ok(ps=63) == SHAPE
 
 
 def _attn(lib, **kw):

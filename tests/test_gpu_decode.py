@@ -247,3 +247,22 @@ def test_errors_raise(gpu_device):
     with pytest.raises(RuntimeError):
         q_bad = torch.empty(st.q.numel() + 8, dtype=torch.bfloat16, device=gpu_device)[1:1 + st.q.numel()]
         pkv.paged_decode_attn(q_bad.view(st.q.shape), st.k_pool, st.v_pool, st.page_table, st.seq_lens, 100)
+
+
+def test_nan_query_gives_nan_rows(gpu_device):
+    """Every score of a row NaN: the row is NaN (as in the oracle), not an empty split's zeros."""
+    inp = inputs(1)
+    q = inp.q.copy()
+    q[1, 2] = W.BF16_NAN
+    st = DeviceStep(inp, gpu_device)
+    st.q = bf16_dev(q, gpu_device)
+    (out, lse), _, _ = st.step(splits=3, want_lse=True)
+    torch.cuda.synchronize()
+    kf, vf = inp.pools_after_store()
+    ref, ref_lse = oracle.paged_decode(q, kf, vf, inp.page_table, inp.seq_lens)
+    g = host_f64_from_bf16(out)
+    assert np.isnan(ref[1, 2]).all() and np.isnan(ref_lse[1, 2])
+    assert np.isnan(g[1, 2]).all() and torch.isnan(lse[1, 2])
+    mask = np.ones(g.shape[:2], bool)
+    mask[1, 2] = False
+    assert np.isfinite(g[mask]).all()
