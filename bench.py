@@ -38,8 +38,8 @@ PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
 # sources when the counters were taken: any edit to them voids the figure.
 COUNTED_TRAFFIC = {
     "workload": "llama3_8b_decode",
-    "sources_sha256": "ab4f1e1011e52a0a785b7eb4c1d7493fa40c496ffdf56cfecd1c7be2c75c0067",
-    "read_bytes": 537580395,    # FETCH_SIZE 262507.5 KiB x (1 GiB / 524322.1 KiB)
+    "sources_sha256": "ff9789c560a208b60b7128cff5f8d3189311ab3701c8ad0bcb67c050a3265fa6",
+    "read_bytes": 537586655,    # FETCH_SIZE 262505.5 KiB x (1 GiB / 524312.0 KiB)
     "write_bytes": 532480,      # WRITE_SIZE 520.0 KiB x (1 GiB / 1048576.0 KiB)
 }
 KERNEL_SOURCES = ["pkv_decode_mfma.hip", "pkv_device.h", "pkv_launch.h"]
