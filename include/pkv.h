@@ -233,6 +233,27 @@ pkv_status pkv_decode_merge(const float *o_partial, const float *lse_partial, in
 int32_t pkv_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
                        int64_t total_tokens, int32_t page_size, int32_t num_cus);
 
+/*
+ * pkv_prefill_plan -- the packed-query work map of a prefill batch (host only).
+ *
+ * Follows: AstrAI "CUDA Kernels", section "Q Scheduling and KV Addressing" (a
+ * packed [total_q, q_heads, head_dim] query tensor is cut into Q tiles of 64
+ * rows per request; each tile knows its request and its tile index within the
+ * request, so a workgroup finds its rows in O(1): for Q lengths [70, 10, 130]
+ * the page prints qo_indptr [0, 70, 80, 210], tile->request [0, 0, 1, 2, 2, 2]
+ * and tile->index [0, 1, 0, 0, 1, 2]).
+ *   q_lens            host int32 [B]: query rows of each request (>= 0)
+ *   qo_indptr         host int32 [B + 1]: exclusive prefix sums of q_lens
+ *   q_tile_to_batch   host int32 [capacity]: request of each tile
+ *   q_tile_to_index   host int32 [capacity]: tile index within its request
+ * Tiles are PKV_PREFILL_TILE_ROWS rows.  Returns the number of tiles; with
+ * either tile array NULL only that number (a size query); PKV_ERR_SHAPE if it
+ * exceeds capacity or a length is negative, PKV_ERR_NULL for missing arrays.
+ */
+#define PKV_PREFILL_TILE_ROWS 64
+int32_t pkv_prefill_plan(const int32_t *q_lens, int32_t B, int32_t *qo_indptr,
+                         int32_t *q_tile_to_batch, int32_t *q_tile_to_index, int32_t capacity);
+
 /* pkv_split_chunk -- positions covered by one split: the smallest multiple of
  * page_size >= ceil(max_seq_len / num_splits).  0 if max_seq_len == 0,
  * PKV_ERR_SHAPE for invalid arguments.  Host only. */

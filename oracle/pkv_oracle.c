@@ -32,6 +32,14 @@
  *            and rotates each (head, dimension pair); its reference is a
  *            complex multiply, i.e. the pair (x[2i], x[2i+1]) is the complex
  *            number x[2i] + i x[2i+1], multiplied by cos + i sin.
+ *   [prefill] AstrAI "CUDA Kernels", sections "Python Wrappers" (is_causal:
+ *            causal mask or none) and "Q Scheduling and KV Addressing" (paged
+ *            prefill over a packed [total_q, q_heads, head_dim] query tensor
+ *            with qo_indptr; each request has its own KV length).  Reading:
+ *            a request's query rows are its last q_len positions, so query
+ *            row j of a request with kv_len tokens sits at position
+ *            kv_len - q_len + j and, with the causal mask, sees positions
+ *            t <= kv_len - q_len + j.
  *   [index]  mini-sglang handbook, "Custom CUDA kernels", section "Moving
  *            whole rows by index": the embedding lookup copies row
  *            ids[t] - start of this rank's vocabulary slice to output row t,
@@ -216,6 +224,65 @@ int oracle_paged_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_
             if (!scores) continue;
             int64_t b = bh / Hq, h = bh % Hq;
             attend(&p, b, h, 0, seq_lens[b], scores, out + bh * D, lse + bh, NULL);
+        }
+        free(scores);
+    }
+    return failed ? -5 : 0;
+}
+
+/* [prefill] Attention of every packed query row.  q [total_q, Hq, D] bf16 with
+ * total_q = qo_indptr[B]; kv_lens[b] tokens of request b in the paged pools.
+ * out [total_q, Hq, D] fp64, lse [total_q, Hq] (natural log).  Returns 0,
+ * -2 on inconsistent sizes (q_len > kv_len, decreasing qo_indptr). */
+int oracle_paged_prefill(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
+                         const int32_t *page_table, const int32_t *kv_lens,
+                         const int32_t *qo_indptr, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                         int64_t P, int64_t max_pages, int causal, double *out, double *lse) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || Hq % Hkv || qo_indptr[0] != 0) return -2;
+    int64_t Lmax = 1;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t ql = qo_indptr[b + 1] - qo_indptr[b];
+        if (ql < 0 || ql > kv_lens[b] || kv_lens[b] > max_pages * P) return -2;
+        if (kv_lens[b] > Lmax) Lmax = kv_lens[b];
+    }
+    const int64_t total_q = qo_indptr[B], G = Hq / Hkv, row = Hkv * D;
+    const double qk_scale = 1.0 / sqrt((double)D);   /* [scale] */
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *scores = malloc((size_t)Lmax * sizeof(double));
+        if (!scores) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t qh = 0; qh < total_q * Hq; ++qh) {
+            if (!scores) continue;
+            const int64_t i = qh / Hq, h = qh % Hq, g = h / G;
+            int64_t b = 0;
+            while (qo_indptr[b + 1] <= i) ++b;          /* the request of packed row i */
+            const int64_t ql = qo_indptr[b + 1] - qo_indptr[b], L = kv_lens[b];
+            const int64_t pos = L - ql + (i - qo_indptr[b]);
+            const int64_t t1 = causal ? pos + 1 : L;    /* positions [0, t1) are seen */
+            const uint16_t *qv = q + (i * Hq + h) * D;
+            double *o = out + qh * D;
+            double m = -INFINITY;
+            for (int64_t t = 0; t < t1; ++t) {
+                const uint16_t *k = k_pool + physical_slot(page_table, max_pages, b, t, P) * row + g * D;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(qv[d]) * bf16_to_double(k[d]);
+                scores[t] = qk_scale * dot;
+                if (scores[t] > m) m = scores[t];
+            }
+            double den = 0.0;
+            for (int64_t t = 0; t < t1; ++t) den += exp(scores[t] - m);
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            for (int64_t t = 0; t < t1; ++t) {
+                const double w = exp(scores[t] - m) / den;
+                const uint16_t *v = v_pool + physical_slot(page_table, max_pages, b, t, P) * row + g * D;
+                for (int64_t d = 0; d < D; ++d) o[d] += w * bf16_to_double(v[d]);
+            }
+            lse[qh] = t1 > 0 ? m + log(den) : -INFINITY;
         }
         free(scores);
     }

@@ -112,6 +112,32 @@ int32_t pkv_split_chunk(int32_t max_seq_len, int32_t num_splits, int32_t page_si
   return int32_t(ceil_div(per, page_size) * page_size);
 }
 
+int32_t pkv_prefill_plan(const int32_t *q_lens, int32_t B, int32_t *qo_indptr,
+                         int32_t *q_tile_to_batch, int32_t *q_tile_to_index, int32_t capacity) {
+  if (B < 0 || capacity < 0) return PKV_ERR_SHAPE;
+  if (B > 0 && (!q_lens || !qo_indptr)) return PKV_ERR_NULL;
+  int64_t total = 0, tiles = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (q_lens[b] < 0) return PKV_ERR_SHAPE;
+    total += q_lens[b];
+    tiles += ceil_div(q_lens[b], PKV_PREFILL_TILE_ROWS);
+  }
+  if (total > INT32_MAX || tiles > INT32_MAX) return PKV_ERR_SHAPE;
+  if (!q_tile_to_batch || !q_tile_to_index) return int32_t(tiles);   // size query
+  if (tiles > capacity) return PKV_ERR_SHAPE;
+  int32_t off = 0, t = 0;
+  if (qo_indptr) qo_indptr[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t i = 0; i * PKV_PREFILL_TILE_ROWS < q_lens[b]; ++i, ++t) {
+      q_tile_to_batch[t] = b;
+      q_tile_to_index[t] = i;
+    }
+    off += q_lens[b];
+    qo_indptr[b + 1] = off;
+  }
+  return t;
+}
+
 int32_t pkv_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
                        int64_t total_tokens, int32_t page_size, int32_t num_cus) {
   if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || max_seq_len < 0 || !is_pow2(page_size) ||

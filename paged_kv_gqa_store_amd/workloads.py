@@ -257,6 +257,70 @@ def bulk_fill_rows(inp: Inputs, seed: int | None = None):
 
 
 @dataclass(frozen=True)
+class PrefillConfig:
+    """A paged prefill batch: request b has kv_lens[b] tokens in the pool, the
+    last q_lens[b] of which are its new query rows (packed over the batch)."""
+    cid: int
+    name: str
+    Hq: int
+    Hkv: int
+    D: int
+    P: int
+    num_pages: int
+    q_lens: tuple
+    kv_lens: tuple
+
+    @property
+    def B(self) -> int:
+        return len(self.q_lens)
+
+    def describe(self) -> str:
+        return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} D={self.D} page_size={self.P} "
+                f"q_lens={list(self.q_lens)[:8]} kv_lens={list(self.kv_lens)[:8]}")
+
+
+PREFILL = {
+    # the page's ragged Q lengths [70, 10, 130], two of them continuing a cached context
+    "ragged_chunks": PrefillConfig(101, "ragged_chunks", 8, 2, 64, 16, 64,
+                                   (70, 10, 130), (70, 300, 200)),
+    # Llama-3-8B-shaped chunked prefill: 1024 new tokens on top of 3072 cached, batch 4
+    "llama3_8b_chunked": PrefillConfig(102, "llama3_8b_chunked", 32, 8, 128, 16, 1100,
+                                       (1024,) * 4, (4096,) * 4),
+    # fresh prompts, q = kv = 2048 (the size of the page's single-batch prefill figure), batch 2
+    "llama3_8b_fresh": PrefillConfig(103, "llama3_8b_fresh", 32, 8, 128, 16, 300,
+                                     (2048,) * 2, (2048,) * 2),
+}
+
+
+def make_prefill_inputs(cfg: PrefillConfig, seed: int | None = None):
+    """(q uint16 [total_q, Hq, D], k_pool, v_pool [num_pages, P, Hkv, D],
+    page_table int32 [B, max_pages], kv_lens int32 [B], qo_indptr int32 [B+1]).
+    The pools and page table are drawn as for a decode step over kv_lens (all
+    positions stored, unowned pages NaN canaries); q ~ N(0, 1) rounded to bf16."""
+    seed = SEED_BASE + cfg.cid if seed is None else seed
+    dcfg = Config(cfg.cid, cfg.name, B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, P=cfg.P,
+                  num_pages=cfg.num_pages, seq_len=None, seq_lens=tuple(cfg.kv_lens))
+    inp = make_inputs(dcfg, seed=seed)
+    k_pool, v_pool = inp.pools_after_store()
+    qo = np.concatenate([[0], np.cumsum(np.asarray(cfg.q_lens, np.int64))]).astype(np.int32)
+    q = _normal_bf16(np.random.SeedSequence(seed + 7), (int(qo[-1]), cfg.Hq, cfg.D))
+    return q, k_pool, v_pool, inp.page_table, np.asarray(cfg.kv_lens, np.int32), qo
+
+
+def prefill_flops(q_lens, kv_lens, Hq: int, D: int, causal: bool = True) -> int:
+    """Multiply-adds x 2 of QK^T and PV over the (query, position) pairs a
+    query row sees: 4 * D flops per pair and q head."""
+    pairs = 0
+    for ql, kl in zip(q_lens, kv_lens):
+        if causal:
+            first = kl - ql + 1            # positions seen by the first query row
+            pairs += ql * first + ql * (ql - 1) // 2
+        else:
+            pairs += ql * kl
+    return 4 * D * Hq * pairs
+
+
+@dataclass(frozen=True)
 class IndexingConfig:
     """A vocabulary-parallel embedding lookup: the table is split into ``shards``
     equal slices of ``vocab / shards`` rows; one rank holds one slice."""
@@ -350,4 +414,5 @@ def sample_rows(cfg: Config, k: int, seed: int = 7) -> np.ndarray:
 __all__ = ["Config", "CONFIGS", "Inputs", "make_inputs", "custom_config", "contiguous_layout",
            "bulk_fill_rows", "kv_bytes", "attention_bytes", "store_bytes", "roofline_us",
            "to_bf16_bits", "bf16_bits_to_f32", "sample_rows", "IndexingConfig", "INDEXING",
-           "make_indexing_inputs", "indexing_bytes", "rope_tables"]
+           "make_indexing_inputs", "indexing_bytes", "rope_tables", "PrefillConfig", "PREFILL",
+           "make_prefill_inputs", "prefill_flops"]

@@ -5,6 +5,7 @@ import ctypes
 import re
 from pathlib import Path
 
+import numpy as np
 import pytest
 
 from oracle import oracle
@@ -29,7 +30,7 @@ def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(["pkv_kv_store", "pkv_paged_decode_attn", "pkv_decode_merge",
                                          "pkv_num_splits", "pkv_split_chunk", "pkv_status_str",
                                          "pkv_indexing", "pkv_kv_store_rope",
-                                         "pkv_paged_decode_attn_rope"])
+                                         "pkv_paged_decode_attn_rope", "pkv_prefill_plan"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -116,6 +117,25 @@ def test_rope_validation(lib):
     assert ok(c=ctypes.c_void_p(516)) == ALIGN
     assert ok(kp=ctypes.c_void_p(258)) == ALIGN
     assert ok(ps=63) == SHAPE
+
+
+def test_prefill_plan_reproduces_the_worked_example(lib):
+    import json
+    g = json.loads((ROOT / "tests" / "golden" / "prefill_schedule_example.json").read_text())
+    assert g["tile_rows"] == 64
+    q_lens = np.array(g["q_lens"], np.int32)
+    B = len(q_lens)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    qo = np.zeros(B + 1, np.int32)
+    assert lib.pkv_prefill_plan(ptr(q_lens), B, ptr(qo), None, None, 0) == 6   # size query
+    tb, ti = np.full(6, -1, np.int32), np.full(6, -1, np.int32)
+    assert lib.pkv_prefill_plan(ptr(q_lens), B, ptr(qo), ptr(tb), ptr(ti), 6) == 6
+    assert qo.tolist() == g["qo_indptr"]
+    assert tb.tolist() == g["q_tile_to_batch"] and ti.tolist() == g["q_tile_to_index"]
+    assert lib.pkv_prefill_plan(ptr(q_lens), B, ptr(qo), ptr(tb), ptr(ti), 5) == SHAPE
+    zero = np.array([0, 64, 65], np.int32)
+    assert lib.pkv_prefill_plan(ptr(zero), 3, ptr(qo), ptr(tb), ptr(ti), 6) == 3   # empty request: no tile
+    assert tb[:3].tolist() == [1, 2, 2] and ti[:3].tolist() == [0, 0, 1]
 
 
 def _attn(lib, **kw):

@@ -14,7 +14,7 @@ SRC = (oracle._SRC).read_text()
 MUTANTS = [
     ("scale dropped", "const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0;"),
     ("scale 1/D", "const double scale = 1.0 / sqrt((double)D);", "const double scale = 1.0 / (double)D;"),
-    ("q head -> wrong kv head", "g = h / G;", "g = h % p->Hkv;"),
+    ("q head -> wrong kv head", "G = p->Hq / p->Hkv, g = h / G;", "G = p->Hq / p->Hkv, g = h % p->Hkv;"),
     ("slot within page off by one", "return page * page_size + t % page_size;",
      "return page * page_size + (t + 1) % page_size;"),
     ("page index ignores position", "page_table[b * max_pages + t / page_size]", "page_table[b * max_pages]"),
@@ -41,6 +41,14 @@ MUTANTS = [
      "const float sn = cos_t[pos * half + i], c = sin_t[pos * half + i];"),
     ("rope pairs halves instead of neighbours", "const float x1 = (float)bf16_to_double(xr[2 * i + 1]);",
      "const float x1 = (float)bf16_to_double(xr[(2 * i + D / 2) % D]);"),
+    ("prefill causal bound off by one", "const int64_t t1 = causal ? pos + 1 : L;",
+     "const int64_t t1 = causal ? pos : L;"),
+    ("prefill query rows aligned to the start", "const int64_t pos = L - ql + (i - qo_indptr[b]);",
+     "const int64_t pos = i - qo_indptr[b];"),
+    ("prefill wrong kv head", "const int64_t i = qh / Hq, h = qh % Hq, g = h / G;",
+     "const int64_t i = qh / Hq, h = qh % Hq, g = h % Hkv;"),
+    ("prefill lse misses the max", "lse[qh] = t1 > 0 ? m + log(den) : -INFINITY;",
+     "lse[qh] = t1 > 0 ? log(den) : -INFINITY;"),
     ("indexing ignores the slice start", "const int64_t local = (int64_t)ids[t] - start;",
      "const int64_t local = (int64_t)ids[t];"),
     ("indexing leaves masked rows unwritten", "memset(out + t * row_bytes, 0, (size_t)row_bytes);",
@@ -58,6 +66,10 @@ PIN_CALLS = [
     (pins.test_merge_closed_forms, ()),
     (pins.test_split_chunk_reading, ()),
     (pins.test_split_then_merge_equals_unsplit, (3,)),
+    (pins.test_prefill_matches_torch_sdpa_with_an_explicit_mask, (True,)),
+    (pins.test_fresh_prefill_is_torch_causal_attention, ()),
+    (pins.test_prefill_single_row_requests_equal_decode, ()),
+    (pins.test_prefill_lse_is_the_log_partition, ()),
     (pins.test_rope_closed_forms, ()),
     (pins.test_rope_within_one_rounding_of_the_exact_rotation, ()),
     (pins.test_rope_matches_torch_complex_multiply, ()),
@@ -70,7 +82,7 @@ PIN_CALLS = [
 
 @pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(tmp_path, name, orig, mut):
-    assert SRC.count(orig) >= 1, f"mutation site for '{name}' not found"
+    assert SRC.count(orig) == 1, f"mutation site for '{name}' not found or not unique"
     src = tmp_path / "mutant.c"
     src.write_text(SRC.replace(orig, mut))
     lib = tmp_path / "libmutant.so"

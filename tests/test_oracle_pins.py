@@ -416,3 +416,71 @@ def test_rope_preserves_relative_position():
     rq = _f64(oracle.rope(q, np.array([100], np.int32), cos, sin, 1))
     rk = _f64(oracle.rope(k, np.array([100], np.int32), cos, sin, 1))
     assert abs(float((rq * rk).sum()) - dots[0]) > 1e-2 * scale
+
+
+# -------------------------------------------------------------- prefill ----
+# AstrAI "CUDA Kernels", sections "Python Wrappers" (is_causal) and "Q
+# Scheduling and KV Addressing" (packed queries with qo_indptr over a paged
+# KV source).  Reading: a request's query rows are its last q_len positions.
+
+def _prefill_case(q_lens, kv_lens, Hq=4, Hkv=2, D=64, P=8, seed=3):
+    cfg = W.PrefillConfig(0, "pin", Hq, Hkv, D, P, -(-sum(kv_lens) // P) + len(kv_lens) + 4,
+                          tuple(q_lens), tuple(kv_lens))
+    return W.make_prefill_inputs(cfg, seed=seed)
+
+
+def _sdpa_request(q, kp, vp, pt, L, qs, qe, Hkv, mask=None, is_causal=False):
+    """torch fp64 scaled_dot_product_attention of one request on gathered K/V;
+    pt is that request's page-table row."""
+    P = kp.shape[1]
+    t = np.arange(L)
+    K = _f64(kp[pt[t // P], t % P])                     # [L, Hkv, D]
+    V = _f64(vp[pt[t // P], t % P])
+    Q = _f64(q[qs:qe])                                  # [ql, Hq, D]
+    G = Q.shape[1] // Hkv
+    Kt = torch.from_numpy(np.repeat(K, G, axis=1)).permute(1, 0, 2)
+    Vt = torch.from_numpy(np.repeat(V, G, axis=1)).permute(1, 0, 2)
+    Qt = torch.from_numpy(Q).permute(1, 0, 2)
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, attn_mask=m, is_causal=is_causal)
+    return o.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_matches_torch_sdpa_with_an_explicit_mask(causal):
+    q_lens, kv_lens = (5, 1, 12, 7), (9, 20, 12, 30)
+    q, kp, vp, pt, kl, qo = _prefill_case(q_lens, kv_lens)
+    out, lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, causal)
+    for b, (ql, L) in enumerate(zip(q_lens, kv_lens)):
+        pos = L - ql + np.arange(ql)
+        mask = (np.arange(L)[None, :] <= pos[:, None]) if causal else None
+        ref = _sdpa_request(q, kp, vp, pt[b], L, qo[b], qo[b + 1], kp.shape[2], mask=mask)
+        assert np.abs(out[qo[b]:qo[b + 1]] - ref).max() <= 1e-12
+
+
+def test_fresh_prefill_is_torch_causal_attention():
+    """q_len == kv_len: the causal mask is torch's own (top-left, no offset)."""
+    q_lens = kv_lens = (17, 40)
+    q, kp, vp, pt, kl, qo = _prefill_case(q_lens, kv_lens, Hq=8, Hkv=1, D=128, P=16)
+    out, _ = oracle.paged_prefill(q, kp, vp, pt, kl, qo, True)
+    for b, L in enumerate(kv_lens):
+        ref = _sdpa_request(q, kp, vp, pt[b], L, qo[b], qo[b + 1], 1, is_causal=True)
+        assert np.abs(out[qo[b]:qo[b + 1]] - ref).max() <= 1e-12
+
+
+def test_prefill_single_row_requests_equal_decode():
+    """One query row per request, at the last position: the decode step's attention."""
+    q_lens, kv_lens = (1, 1, 1), (37, 100, 5)
+    q, kp, vp, pt, kl, qo = _prefill_case(q_lens, kv_lens, Hq=4, Hkv=1, D=64, P=16)
+    out, lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, True)
+    dout, dlse = oracle.paged_decode(q, kp, vp, pt, kl)
+    assert np.abs(out - dout).max() <= 1e-12 and np.abs(lse - dlse).max() <= 1e-12
+
+
+def test_prefill_lse_is_the_log_partition():
+    q_lens, kv_lens = (3,), (11,)
+    q, kp, vp, pt, kl, qo = _prefill_case(q_lens, kv_lens, Hq=2, Hkv=2)
+    _, lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, False)
+    K = _f64(kp[pt[0, np.arange(11) // 8], np.arange(11) % 8])
+    s = np.einsum("qhd,thd->qht", _f64(q), K) / math.sqrt(64)
+    assert np.abs(lse - np.log(np.exp(s).sum(-1))).max() <= 1e-12
