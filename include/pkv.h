@@ -5,6 +5,8 @@
  *   pkv_kv_store          scatter the step's new K/V rows into the page pool
  *   pkv_kv_store_rope     the store with K rows rotated by a rotary embedding on the way
  *   pkv_paged_decode_attn_rope  the attention with q rotated in its prologue
+ *   pkv_paged_prefill_attn  attention of packed multi-token queries (prefill)
+ *   pkv_prefill_plan      the Q-tile work map of a prefill batch (host only)
  *   pkv_indexing          row gather from a vocabulary slice (embedding lookup)
  *   pkv_paged_decode_attn split-KV attention through the page table -> partials
  *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
@@ -115,6 +117,44 @@ pkv_status pkv_kv_store_rope(void *k_pool, void *v_pool, int64_t num_slots,
                              int32_t Hkv, int32_t D, const int32_t *positions,
                              const float *rope_cos, const float *rope_sin, int32_t rope_rows,
                              void *stream);
+
+/*
+ * pkv_paged_prefill_attn -- attention of packed multi-token queries (a prefill
+ * or a prefill chunk) over the paged pool.
+ *
+ * Follows: AstrAI "CUDA Kernels", section "Q Scheduling and KV Addressing"
+ * (packed queries, the Q tile work map of pkv_prefill_plan, paged KV
+ * addressing, GQA head packing) and section "Python Wrappers" (is_causal; scale
+ * 1/sqrt(head_dim)).  Request b has kv_lens[b] tokens in the pool (its new ones
+ * already stored) and query rows qo_indptr[b] .. qo_indptr[b+1]-1, which are
+ * its last q_len = qo_indptr[b+1] - qo_indptr[b] positions: row j of the
+ * request sits at position p_j = kv_lens[b] - q_len + j.  For q head h
+ * (kv head g = h / (Hq/Hkv)):
+ *     x_t = scale * <q[row, h, :], K[phys(b, t), g, :]>   over t in T_j
+ *     out[row, h, :] = sum_{t in T_j} softmax(x)_t V[phys(b, t), g, :]
+ *     lse[row, h] = ln sum_{t in T_j} exp(x_t)          (if lse != NULL)
+ * with T_j = [0, p_j] when causal != 0, else [0, kv_lens[b]).  fp32 softmax
+ * statistics and accumulation; the probabilities enter the P.V product as
+ * bf16 (the matrix-core operand); out is bf16 (RNE).
+ *   q            device bf16 [total_q, Hq, D], 16-byte aligned
+ *   qo_indptr    device int32 [B + 1];  q_tile_to_batch / q_tile_to_index
+ *                device int32 [num_q_tiles], as built by pkv_prefill_plan
+ *   kv_lens      device int32 [B];  pools and page_table as for decode
+ *   out          device bf16 [total_q, Hq, D], 8-byte aligned
+ *   D in {64, 128}; Hq/Hkv in {1, 2, 4, 8}; page_size a power of two <= 1024.
+ * Preconditions (device): q_len <= kv_lens[b] <= max_pages_per_seq*page_size
+ * and a work map built for these qo_indptr.  Rows and positions outside
+ * total_q and the page table are never touched; a row that sees no position
+ * comes out NaN, and so does a row that would use a page id outside the pool.
+ */
+pkv_status pkv_paged_prefill_attn(const void *q, const void *k_pool, const void *v_pool,
+                                  const int32_t *page_table, const int32_t *kv_lens,
+                                  const int32_t *qo_indptr, const int32_t *q_tile_to_batch,
+                                  const int32_t *q_tile_to_index, int32_t num_q_tiles,
+                                  int32_t total_q, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t page_size, int32_t num_pages, int32_t max_pages_per_seq,
+                                  int32_t causal, float scale, void *out, float *lse,
+                                  void *stream);
 
 /*
  * pkv_paged_decode_attn_rope -- pkv_paged_decode_attn with q rotated by the

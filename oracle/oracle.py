@@ -84,7 +84,7 @@ def _load(path: Path | None = None):
         lib.oracle_merge.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p]
         lib.oracle_merge.restype = None
         lib.oracle_paged_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
-                                             ctypes.c_int, _p, _p]
+                                             ctypes.c_int, _p, _i64, _p, _p]
         lib.oracle_paged_prefill.restype = ctypes.c_int
         lib.oracle_rope.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _i64]
         lib.oracle_rope.restype = ctypes.c_int
@@ -135,11 +135,12 @@ def kv_store(k_pool, v_pool, k_new, v_new, slot_mapping, row_elems=None):
     return k_out, v_out
 
 
-def paged_prefill(q, k_pool, v_pool, page_table, kv_lens, qo_indptr, causal: bool = True):
+def paged_prefill(q, k_pool, v_pool, page_table, kv_lens, qo_indptr, causal: bool = True, rows=None):
     """Prefill attention of packed query rows.  q uint16 ``[total_q, Hq, D]``,
     pools ``[num_pages, P, Hkv, D]``, page_table int32 ``[B, max_pages]``,
     kv_lens int32 ``[B]``, qo_indptr int32 ``[B+1]``.  Returns
-    (out fp64 ``[total_q, Hq, D]``, lse fp64 ``[total_q, Hq]``)."""
+    (out fp64 ``[total_q, Hq, D]``, lse fp64 ``[total_q, Hq]``), or with
+    ``rows`` (pairs (packed row, head)) just those: ``[n, D]``, ``[n]``."""
     q = _c(q, np.uint16)
     k_pool = _c(k_pool, np.uint16)
     v_pool = _c(v_pool, np.uint16)
@@ -150,10 +151,19 @@ def paged_prefill(q, k_pool, v_pool, page_table, kv_lens, qo_indptr, causal: boo
     num_pages, P, Hkv, D2 = k_pool.shape
     B = kl.shape[0]
     assert D2 == D and qo.shape == (B + 1,) and int(qo[-1]) == total_q and pt.shape[0] == B
-    out = np.empty((total_q, Hq, D), np.float64)
-    lse = np.empty((total_q, Hq), np.float64)
+    if rows is None:
+        out = np.empty((total_q, Hq, D), np.float64)
+        lse = np.empty((total_q, Hq), np.float64)
+        r_ptr, n = None, 0
+    else:
+        r = _c(rows, np.int64).reshape(-1, 2)
+        n = r.shape[0]
+        out = np.empty((n, D), np.float64)
+        lse = np.empty((n,), np.float64)
+        r_ptr = _ptr(r)
     rc = _load().oracle_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(pt), _ptr(kl), _ptr(qo),
-                                      B, Hq, Hkv, D, P, pt.shape[1], int(bool(causal)), _ptr(out), _ptr(lse))
+                                      B, Hq, Hkv, D, P, pt.shape[1], int(bool(causal)), r_ptr, n,
+                                      _ptr(out), _ptr(lse))
     _check(rc, "paged_prefill")
     return out, lse
 

@@ -237,7 +237,8 @@ int oracle_paged_decode(const uint16_t *q, const uint16_t *k_pool, const uint16_
 int oracle_paged_prefill(const uint16_t *q, const uint16_t *k_pool, const uint16_t *v_pool,
                          const int32_t *page_table, const int32_t *kv_lens,
                          const int32_t *qo_indptr, int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
-                         int64_t P, int64_t max_pages, int causal, double *out, double *lse) {
+                         int64_t P, int64_t max_pages, int causal, const int64_t *rows,
+                         int64_t n_rows, double *out, double *lse) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || Hq % Hkv || qo_indptr[0] != 0) return -2;
     int64_t Lmax = 1;
     for (int64_t b = 0; b < B; ++b) {
@@ -256,8 +257,11 @@ int oracle_paged_prefill(const uint16_t *q, const uint16_t *k_pool, const uint16
             failed = 1;
         }
 #pragma omp for schedule(dynamic, 4)
-        for (int64_t qh = 0; qh < total_q * Hq; ++qh) {
+        for (int64_t n = 0; n < (rows ? n_rows : total_q * Hq); ++n) {
             if (!scores) continue;
+            /* output slot n holds packed row i, head h (all of them in order, or rows[n]) */
+            const int64_t qh = rows ? rows[2 * n] * Hq + rows[2 * n + 1] : n;
+            if (qh < 0 || qh >= total_q * Hq) continue;
             const int64_t i = qh / Hq, h = qh % Hq, g = h / G;
             int64_t b = 0;
             while (qo_indptr[b + 1] <= i) ++b;          /* the request of packed row i */
@@ -265,7 +269,7 @@ int oracle_paged_prefill(const uint16_t *q, const uint16_t *k_pool, const uint16
             const int64_t pos = L - ql + (i - qo_indptr[b]);
             const int64_t t1 = causal ? pos + 1 : L;    /* positions [0, t1) are seen */
             const uint16_t *qv = q + (i * Hq + h) * D;
-            double *o = out + qh * D;
+            double *o = out + n * D;
             double m = -INFINITY;
             for (int64_t t = 0; t < t1; ++t) {
                 const uint16_t *k = k_pool + physical_slot(page_table, max_pages, b, t, P) * row + g * D;
@@ -282,7 +286,7 @@ int oracle_paged_prefill(const uint16_t *q, const uint16_t *k_pool, const uint16
                 const uint16_t *v = v_pool + physical_slot(page_table, max_pages, b, t, P) * row + g * D;
                 for (int64_t d = 0; d < D; ++d) o[d] += w * bf16_to_double(v[d]);
             }
-            lse[qh] = t1 > 0 ? m + log(den) : -INFINITY;
+            lse[n] = t1 > 0 ? m + log(den) : -INFINITY;
         }
         free(scores);
     }

@@ -7,7 +7,8 @@ One decode step is three hand-written HIP kernels behind a C ABI
 * ``paged_decode_attn``  split-KV attention over pages found through a page table;
 * ``decode_merge``       log-sum-exp merge of the split partials;
 
-plus ``kv_store_rope`` (the store with K rotated by a rotary embedding on the
+plus ``paged_prefill_attn`` (packed multi-token queries over the same pool,
+with the ``prefill_plan`` work map), ``kv_store_rope`` (the store with K rotated by a rotary embedding on the
 way, and ``paged_decode_attn(..., q_positions=...)`` rotating q in the
 attention prologue) and ``indexing``, a row gather from one rank's slice of a
 vocabulary-parallel embedding table, on the same row-move kernel design as
@@ -19,6 +20,6 @@ every op raises ``RuntimeError`` if ``libpkv.so`` is missing: there is no
 fallback implementation.
 """
 from .ops import (  # noqa: F401
-    decode_merge, decode_step, indexing, kv_store, kv_store_rope, num_splits, paged_decode_attn,
-    split_chunk, workspace,
+    PrefillPlan, decode_merge, decode_step, indexing, kv_store, kv_store_rope, num_splits,
+    paged_decode_attn, paged_prefill_attn, prefill_plan, split_chunk, workspace,
 )

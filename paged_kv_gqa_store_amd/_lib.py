@@ -27,6 +27,8 @@ SIGNATURES = [
                                      _i32, _i32, _f32, _p, _p, _p]),
     ("pkv_decode_merge", _i32, [_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
     ("pkv_prefill_plan", _i32, [_p, _i32, _p, _p, _p, _i32]),
+    ("pkv_paged_prefill_attn", _i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _i32, _i32, _i32, _i32, _f32, _p, _p, _p]),
     ("pkv_num_splits", _i32, [_i32, _i32, _i32, _i32, _i64, _i32, _i32]),
     ("pkv_split_chunk", _i32, [_i32, _i32, _i32]),
     ("pkv_status_str", ctypes.c_char_p, [_i32]),

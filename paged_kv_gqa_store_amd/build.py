@@ -17,7 +17,7 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libpkv.so"
-SOURCES = ["pkv_api.hip", "pkv_store.hip", "pkv_decode.hip", "pkv_decode_mfma.hip"]
+SOURCES = ["pkv_api.hip", "pkv_store.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -265,6 +265,60 @@ pkv_status pkv_paged_decode_attn_rope(const void *q, const void *k_pool, const v
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+pkv_status pkv_paged_prefill_attn(const void *q, const void *k_pool, const void *v_pool,
+                                  const int32_t *page_table, const int32_t *kv_lens,
+                                  const int32_t *qo_indptr, const int32_t *q_tile_to_batch,
+                                  const int32_t *q_tile_to_index, int32_t num_q_tiles,
+                                  int32_t total_q, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                  int32_t num_pages, int32_t max_pages_per_seq, int32_t causal,
+                                  float scale, void *out, float *lse, void *stream) {
+  if (B < 0 || num_q_tiles < 0 || total_q < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 ||
+      max_pages_per_seq < 1)
+    return PKV_ERR_SHAPE;
+  if (Hq % Hkv) return PKV_ERR_SHAPE;
+  const int G = Hq / Hkv;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size > 1024) return PKV_ERR_UNSUPPORTED;
+  if (B > 65535 || Hkv > 65535 || int64_t(num_q_tiles) * 4 > int64_t(INT32_MAX)) return PKV_ERR_SHAPE;
+  if (int64_t(num_pages) * page_size > (int64_t(1) << 31)) return PKV_ERR_SHAPE;
+  if (int64_t(max_pages_per_seq) * page_size > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return PKV_ERR_SHAPE;
+  if (B == 0 || num_q_tiles == 0 || total_q == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !page_table || !kv_lens || !qo_indptr || !q_tile_to_batch ||
+      !q_tile_to_index || !out)
+    return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      (reinterpret_cast<uintptr_t>(out) & 7u))
+    return PKV_ERR_ALIGN;
+  pkv::PrefillParams p;
+  p.q = static_cast<const uint16_t *>(q);
+  p.k_pool = static_cast<const uint16_t *>(k_pool);
+  p.v_pool = static_cast<const uint16_t *>(v_pool);
+  p.page_table = page_table;
+  p.kv_lens = kv_lens;
+  p.qo_indptr = qo_indptr;
+  p.tile_to_batch = q_tile_to_batch;
+  p.tile_to_index = q_tile_to_index;
+  p.out = static_cast<uint16_t *>(out);
+  p.lse = lse;
+  p.num_q_tiles = num_q_tiles;
+  p.total_q = total_q;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.G = G;
+  p.page_log2 = log2_exact(page_size);
+  p.num_pages = num_pages;
+  p.max_pages = max_pages_per_seq;
+  p.causal = causal ? 1 : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pkv::launch_paged_prefill(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 pkv_status pkv_decode_merge(const float *o_partial, const float *lse_partial, int32_t B,
                             int32_t Hq, int32_t D, int32_t num_splits, void *out, float *lse_out,
                             void *stream) {

@@ -1,0 +1,247 @@
+// Paged prefill attention: packed multi-token queries over the paged pool.
+//
+// Follows AstrAI "CUDA Kernels": section "Q Scheduling and KV Addressing"
+// (packed [total_q, q_heads, head_dim] queries cut into 64-row Q tiles with a
+// tile -> (request, tile index) map; the paged KV source only translates
+// logical positions; HB = min(G, waves) q heads of one kv-head group packed
+// per workgroup so a K/V tile is read once for all of them; the grid is
+// (num_q_tiles * HB) x (kv_heads * ceil(G / HB))) and section "Python
+// Wrappers" (is_causal; scale 1/sqrt(head_dim)).  A request's query rows are
+// its last q_len positions: with the causal mask, row j of a request with
+// kv_len tokens sees positions <= kv_len - q_len + j.
+//
+// gfx950 design, per wave: 16 query rows of one q head.
+//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16 with A = a 16-token block of the
+//                  K tile (LDS, row-major) and B = Q^T (registers, loaded once):
+//                  the output puts one query row per lane (lane & 15) and 4
+//                  tokens per register group, so the online softmax of a row
+//                  reduces over 16 registers and the 4 lane groups.
+//   O^T += V^T P^T the probabilities are already in the B-operand layout of
+//                  P^T (8 tokens of the lane's row); A = V^T is read from a
+//                  transposed V tile that the workgroup writes into LDS while
+//                  staging it.  P is rounded to bf16 for the matrix core;
+//                  the accumulators and the softmax statistics stay fp32.
+// The workgroup's 4 waves share each 64-token K/V tile; the next tile's
+// global loads are in flight while the current one is computed.
+#include <math.h>
+
+#include "pkv.h"
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kQTile = PKV_PREFILL_TILE_ROWS;   // query rows per host tile
+constexpr int kKT = 64;                         // tokens per K/V tile
+constexpr int kThreads = 256;                   // 4 waves
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int D, int HB>
+__global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p) {
+  constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension
+  constexpr int DB = D / 16;                 // 16-dim blocks of the output
+  constexpr int CPT = D / 8;                 // 16-byte chunks per token row
+  constexpr int TPS = kThreads / CPT;        // tokens staged per pass
+  constexpr int PASSES = kKT / TPS;
+  constexpr int TCH = 4 / HB;                // 16-row chunks per workgroup
+  constexpr int KPITCH = D * 2 + 16;         // bytes per K row in LDS (padded)
+  constexpr int VPITCH = kKT * 2 + 16;       // bytes per V^T row (one dimension) in LDS
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k[kKT * KPITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_vt[D * VPITCH];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int host_tile = blockIdx.x / HB, chunk = blockIdx.x % HB;
+  const int hgroups = (p.G + HB - 1) / HB;
+  const int g = blockIdx.y / hgroups, hg = blockIdx.y % hgroups;
+  const int b = p.tile_to_batch[host_tile];
+  if (unsigned(b) >= unsigned(p.B)) return;                   // whole workgroup
+  // rows past total_q and positions past the page table are never touched
+  const int q0 = min(max(p.qo_indptr[b], 0), p.total_q);
+  const int q_len = min(p.qo_indptr[b + 1], p.total_q) - q0;
+  const int kv_len = min(max(p.kv_lens[b], 0), p.max_pages << p.page_log2);
+  // rows of this workgroup within the request, and of this wave
+  const int wg_row0 = p.tile_to_index[host_tile] * kQTile + chunk * (kQTile / HB);
+  const int wg_rows = min(kQTile / HB, q_len - wg_row0);
+  if (wg_row0 < 0 || wg_rows <= 0) return;                   // whole workgroup
+  const int head_slot = wave / TCH;
+  const int h_in_group = hg * HB + head_slot;
+  const bool head_ok = h_in_group < p.G;
+  const int h = g * p.G + (head_ok ? h_in_group : 0);
+  const int row0 = wg_row0 + (wave % TCH) * 16;              // first row of this wave
+  const int my_row = row0 + (lane & 15);                      // this lane's query row
+  const bool row_ok = head_ok && my_row < q_len;
+  const int pos_base = kv_len - q_len;                        // position of row 0
+  const int my_pos = pos_base + my_row;
+  // positions the workgroup needs: [0, kv_end)
+  const int kv_end = p.causal ? min(kv_len, pos_base + wg_row0 + wg_rows) : kv_len;
+  const int log2P = p.page_log2, pmask = (1 << log2P) - 1;
+  const int32_t *pt = p.page_table + size_t(b) * p.max_pages;
+  const size_t row_stride = size_t(p.Hkv) * D;
+
+  // Q^T as the B operand: lane = query row (lane & 15), dims 32j + 8(lane >> 4)
+  bf16x8 qb[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (row_ok) w = *reinterpret_cast<const u32x4 *>(p.q + (size_t(q0 + my_row) * p.Hq + h) * D + 32 * j + 8 * (lane >> 4));
+    qb[j] = as_bf16x8(w);
+  }
+
+  float m = -INFINITY, l = 0.f;   // running max (log2 domain) and this lane's partial sum
+  f32x4 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // staging: thread -> (token tok0 + TPS * pass, 16-byte chunk c)
+  const int c = threadIdx.x % CPT, tok0 = threadIdx.x / CPT;
+  u32x4 kreg[PASSES], vreg[PASSES];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int t = t0 + tok0 + TPS * ps;
+      kreg[ps] = u32x4{0u, 0u, 0u, 0u};
+      vreg[ps] = u32x4{0u, 0u, 0u, 0u};
+      if (t < kv_end) {
+        const int raw = pt[t >> log2P];
+        const int pid = unsigned(raw) < unsigned(p.num_pages) ? raw : 0;
+        const size_t row = (size_t(pid) << log2P) + (t & pmask);
+        const size_t off = row * row_stride + size_t(g) * D + 8 * c;
+        kreg[ps] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k_pool + off));
+        vreg[ps] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.v_pool + off));
+        if (unsigned(raw) >= unsigned(p.num_pages)) {   // a bad page id poisons the row
+          kreg[ps] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+          vreg[ps] = kreg[ps];
+        }
+      }
+    }
+  };
+  auto stage_tile = [&]() {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int tt = tok0 + TPS * ps;
+      *reinterpret_cast<u32x4 *>(sm_k + tt * KPITCH + 16 * c) = kreg[ps];
+      // V^T: dimension 8c + e, token tt
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned w = vreg[ps][e];
+        *reinterpret_cast<uint16_t *>(sm_vt + (8 * c + 2 * e) * VPITCH + 2 * tt) = uint16_t(w & 0xffffu);
+        *reinterpret_cast<uint16_t *>(sm_vt + (8 * c + 2 * e + 1) * VPITCH + 2 * tt) = uint16_t(w >> 16);
+      }
+    }
+  };
+
+  const int ntiles = (kv_end + kKT - 1) / kKT;
+  load_tile(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    __syncthreads();                 // the previous tile's LDS reads are done
+    stage_tile();
+    __syncthreads();
+    if (kt + 1 < ntiles) load_tile((kt + 1) * kKT);   // in flight while this tile is computed
+    const int t0 = kt * kKT;
+
+    // S^T for 4 blocks of 16 tokens: lane holds tokens 16mb + 4(lane >> 4) + r of row lane & 15
+    f32x4 s[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(sm_k + (16 * mb + (lane & 15)) * KPITCH + 2 * (32 * j + 8 * (lane >> 4)));
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
+      }
+    }
+    // scale (log2 domain), mask, tile max of this lane's row
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = t0 + 16 * mb + 4 * (lane >> 4) + r;
+        const bool seen = pos < kv_end && (!p.causal || pos <= my_pos);
+        const float x = seen ? s[mb][r] * p.scale_log2 : -INFINITY;
+        s[mb][r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(m, tmax);
+    const float alpha = (m == mn) ? 1.f : fast_exp2(m - mn);
+    m = mn;
+    l *= alpha;
+    // probabilities in the B layout of P^T: k-slot 8(lane >> 4) + i <-> token
+    // 32kb + 4(lane >> 4) + i (i < 4) or 32kb + 16 + 4(lane >> 4) + i - 4
+    u32x4 pb[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const float x0 = s[2 * kb + half][r], x1 = s[2 * kb + half][r + 1];
+          const float p0 = mn == -INFINITY ? 0.f : fast_exp2(x0 - mn);
+          const float p1 = mn == -INFINITY ? 0.f : fast_exp2(x1 - mn);
+          l += p0 + p1;
+          pb[kb][2 * half + r / 2] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
+        }
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] *= alpha;
+    // O^T += V^T P^T over the tile's two 32-token k-blocks
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < DB; ++i) {
+        const unsigned char *vrow = sm_vt + (16 * i + (lane & 15)) * VPITCH;
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 2 * (32 * kb + 4 * (lane >> 4)));
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 2 * (32 * kb + 16 + 4 * (lane >> 4)));
+        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+        o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb[kb]), o[i], 0, 0, 0);
+      }
+    }
+  }
+
+  // row sums over the 4 lane groups, then the output rows
+  float lsum = l;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (!row_ok) return;
+  const float inv = 1.f / lsum;
+  uint16_t *orow = p.out + (size_t(q0 + my_row) * p.Hq + h) * D;
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    u32x2 w;
+    w[0] = f32_to_bf16_rne(o[i][0] * inv) | (f32_to_bf16_rne(o[i][1] * inv) << 16);
+    w[1] = f32_to_bf16_rne(o[i][2] * inv) | (f32_to_bf16_rne(o[i][3] * inv) << 16);
+    *reinterpret_cast<u32x2 *>(orow + 16 * i + 4 * (lane >> 4)) = w;
+  }
+  if (p.lse && lane < 16) p.lse[size_t(q0 + my_row) * p.Hq + h] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
+}
+
+template <int D, int HB>
+hipError_t launch(const PrefillParams &p, hipStream_t stream) {
+  const int hgroups = (p.G + HB - 1) / HB;
+  const dim3 grid{unsigned(p.num_q_tiles * HB), unsigned(p.Hkv * hgroups)}, block{kThreads};
+  hipLaunchKernelGGL((paged_prefill_kernel<D, HB>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_paged_prefill(const PrefillParams &p, hipStream_t stream) {
+  const int HB = p.G < 4 ? p.G : 4;
+#define PKV_CASE(DD, HH) \
+  if (p.D == DD && HB == HH) return launch<DD, HH>(p, stream);
+  PKV_CASE(64, 1) PKV_CASE(64, 2) PKV_CASE(64, 4)
+  PKV_CASE(128, 1) PKV_CASE(128, 2) PKV_CASE(128, 4)
+#undef PKV_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

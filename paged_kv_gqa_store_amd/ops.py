@@ -7,8 +7,11 @@ in the library's HIP kernels; PyTorch only provides device memory and streams.
 """
 from __future__ import annotations
 
+import ctypes
 import math
+from typing import NamedTuple
 
+import numpy as np
 import torch
 
 from ._lib import check, lib
@@ -149,6 +152,70 @@ def kv_store_rope(k_pool, v_pool, k_new, v_new, slot_mapping, positions, rope_co
                                  positions.data_ptr(), rope_cos.data_ptr(), rope_sin.data_ptr(),
                                  rope_cos.shape[0], _stream(kp))
     check(st, "pkv_kv_store_rope")
+
+
+class PrefillPlan(NamedTuple):
+    """The packed-query work map of a prefill batch (``pkv_prefill_plan``),
+    on the device: ``qo_indptr`` int32 ``[B+1]``, ``tile_to_batch`` and
+    ``tile_to_index`` int32 ``[num_tiles]``."""
+    qo_indptr: torch.Tensor
+    tile_to_batch: torch.Tensor
+    tile_to_index: torch.Tensor
+    num_tiles: int
+    total_q: int
+
+
+def prefill_plan(q_lens, device) -> PrefillPlan:
+    """Build the work map for query lengths ``q_lens`` (host sequence of ints)
+    with the library's host planner and copy it to ``device``."""
+    ql = np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
+    B = ql.shape[0]
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    qo = np.zeros(B + 1, np.int32)
+    n = lib().pkv_prefill_plan(ptr(ql), B, ptr(qo), None, None, 0)
+    check(min(n, 0), "pkv_prefill_plan")
+    tb, ti = np.zeros(max(n, 1), np.int32), np.zeros(max(n, 1), np.int32)
+    n = lib().pkv_prefill_plan(ptr(ql), B, ptr(qo), ptr(tb), ptr(ti), tb.shape[0])
+    check(min(n, 0), "pkv_prefill_plan")
+    dev = lambda a: torch.from_numpy(a).to(device)
+    return PrefillPlan(dev(qo), dev(tb[:max(n, 1)]), dev(ti[:max(n, 1)]), int(n), int(qo[-1]))
+
+
+def paged_prefill_attn(q, k_pool, v_pool, page_table, kv_lens, plan: PrefillPlan, causal: bool = True,
+                       scale: float | None = None, out=None, want_lse: bool = False):
+    """Attention of packed queries ``q`` ``[total_q, Hq, D]`` bf16 over the paged
+    pool; request b's rows are its last ``q_len`` positions of ``kv_lens[b]``.
+    Returns ``out`` ``[total_q, Hq, D]`` bf16 (and lse fp32 ``[total_q, Hq]``)."""
+    _on_gpu(q, k_pool, v_pool, page_table, kv_lens, plan.qo_indptr)
+    _require(q.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
+             "q and the pools must be bfloat16")
+    _require(q.dim() == 3 and q.is_contiguous() and q.shape[0] == plan.total_q,
+             "q must be contiguous [total_q, Hq, D] matching the plan")
+    _require(k_pool.dim() == 4 and k_pool.is_contiguous() and v_pool.is_contiguous()
+             and v_pool.shape == k_pool.shape, "pools must be contiguous [num_pages,P,Hkv,D]")
+    _require(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous(),
+             "page_table must be contiguous int32 [B,max_pages]")
+    B = page_table.shape[0]
+    _require(kv_lens.dtype == torch.int32 and kv_lens.shape == (B,) and kv_lens.is_contiguous(),
+             "kv_lens must be contiguous int32 [B]")
+    _require(plan.qo_indptr.shape == (B + 1,), "plan built for another batch size")
+    total_q, Hq, D = q.shape
+    num_pages, P, Hkv, D2 = k_pool.shape
+    _require(D2 == D, "head sizes differ")
+    if out is None:
+        out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _require(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous(),
+             "out must be contiguous bf16 like q")
+    lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    st = lib().pkv_paged_prefill_attn(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                      page_table.data_ptr(), kv_lens.data_ptr(), plan.qo_indptr.data_ptr(),
+                                      plan.tile_to_batch.data_ptr(), plan.tile_to_index.data_ptr(),
+                                      plan.num_tiles, total_q, B, Hq, Hkv, D, P, num_pages,
+                                      page_table.shape[1], int(bool(causal)), scale, out.data_ptr(),
+                                      lse.data_ptr() if lse is not None else None, _stream(q))
+    check(st, "pkv_paged_prefill_attn")
+    return (out, lse) if want_lse else out
 
 
 def workspace(B: int, Hq: int, D: int, splits: int, device) -> tuple[torch.Tensor, torch.Tensor]:

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(["pkv_kv_store", "pkv_paged_decode_attn", "pkv_decode_merge",
                                          "pkv_num_splits", "pkv_split_chunk", "pkv_status_str",
                                          "pkv_indexing", "pkv_kv_store_rope",
-                                         "pkv_paged_decode_attn_rope", "pkv_prefill_plan"])
+                                         "pkv_paged_decode_attn_rope", "pkv_prefill_plan",
+                                         "pkv_paged_prefill_attn"])
 
 
 def test_library_exports_every_declared_symbol(lib):

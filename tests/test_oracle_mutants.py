@@ -47,8 +47,8 @@ MUTANTS = [
      "const int64_t pos = i - qo_indptr[b];"),
     ("prefill wrong kv head", "const int64_t i = qh / Hq, h = qh % Hq, g = h / G;",
      "const int64_t i = qh / Hq, h = qh % Hq, g = h % Hkv;"),
-    ("prefill lse misses the max", "lse[qh] = t1 > 0 ? m + log(den) : -INFINITY;",
-     "lse[qh] = t1 > 0 ? log(den) : -INFINITY;"),
+    ("prefill lse misses the max", "lse[n] = t1 > 0 ? m + log(den) : -INFINITY;",
+     "lse[n] = t1 > 0 ? log(den) : -INFINITY;"),
     ("indexing ignores the slice start", "const int64_t local = (int64_t)ids[t] - start;",
      "const int64_t local = (int64_t)ids[t];"),
     ("indexing leaves masked rows unwritten", "memset(out + t * row_bytes, 0, (size_t)row_bytes);",

@@ -484,3 +484,12 @@ def test_prefill_lse_is_the_log_partition():
     K = _f64(kp[pt[0, np.arange(11) // 8], np.arange(11) % 8])
     s = np.einsum("qhd,thd->qht", _f64(q), K) / math.sqrt(64)
     assert np.abs(lse - np.log(np.exp(s).sum(-1))).max() <= 1e-12
+
+
+def test_prefill_rows_mode_equals_full_mode():
+    q, kp, vp, pt, kl, qo = _prefill_case((5, 9), (12, 9))
+    full, flse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, True)
+    rows = [(0, 0), (4, 3), (13, 1), (7, 2)]
+    out, lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, True, rows=rows)
+    for n, (i, h) in enumerate(rows):
+        assert (out[n] == full[i, h]).all() and lse[n] == flse[i, h]
