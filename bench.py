@@ -30,6 +30,7 @@ import time
 import numpy as np
 
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, published
 
 # HBM bytes per launch of the decode kernel on the default workload, counted by
 # rocprofv3 in two runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
@@ -75,7 +76,8 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="report the eagerly launched steps instead of one graph replay of K steps")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the secondary measurements (rotary store and attention, embedding row gather)")
+                    help="skip the secondary measurements (rotary store and attention, prefill, "
+                         "embedding row gather)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size reference "
                          "for the HBM byte counters of a profiler run)")
@@ -112,6 +114,22 @@ def measure_extras(args, pkv, W, dev, to_bf16, to_i32) -> dict:
     """Secondary rows of the path, each on its own synthetic workload."""
     import torch
     extras = {}
+    for name in ("llama3_8b_chunked", "llama3_8b_fresh"):
+        pcfg = W.PREFILL[name]
+        q, kp, vp, pt, kl, qo = W.make_prefill_inputs(pcfg)
+        plan = pkv.prefill_plan(np.diff(qo), dev)
+        qd, kd, vd, ptd, kld = to_bf16(q), to_bf16(kp), to_bf16(vp), to_i32(pt), to_i32(kl)
+        out = torch.empty_like(qd)
+        us = time_launches(lambda i: pkv.paged_prefill_attn(qd, kd, vd, ptd, kld, plan, out=out), reps=20)
+        flops = W.prefill_flops(pcfg.q_lens, pcfg.kv_lens, pcfg.Hq, pcfg.D, causal=True)
+        tflops = flops / (us * 1e-6) / 1e12
+        extras["prefill_" + name] = {
+            "op": "paged_prefill_attn (causal)", "us": round(us, 2), "TFLOPs": round(tflops, 1),
+            "pct_of_bf16_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "flops": flops,
+            "shape": pcfg.describe()}
+        log(f"[bench] prefill {name}: {us:.1f} us, {tflops:.0f} TFLOP/s "
+            f"({tflops / PEAK_BF16_TFLOPS:.1%} of {PEAK_BF16_TFLOPS:.0f} bf16 dense)")
+        del qd, kd, vd, out
     for name in ("llama3_8b_embed_prefill", "llama3_8b_embed_decode"):
         icfg = W.INDEXING[name]
         table, ids, start = W.make_indexing_inputs(icfg, rank=0)
