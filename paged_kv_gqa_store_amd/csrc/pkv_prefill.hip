@@ -10,7 +10,8 @@
 // its last q_len positions: with the causal mask, row j of a request with
 // kv_len tokens sees positions <= kv_len - q_len + j.
 //
-// gfx950 design, per wave: 16 query rows of one q head.
+// gfx950 design, per wave: 16 or 32 query rows (one or two 16-row blocks) of
+// one q head.
 //   S^T = K Q^T    v_mfma_f32_16x16x32_bf16 with A = a 16-token block of the
 //                  K tile (LDS, row-major) and B = Q^T (registers, loaded once):
 //                  the output puts one query row per lane (lane & 15) and 4
@@ -43,14 +44,32 @@ constexpr int kThreads = 256;                   // 4 waves
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int D, int HB>
+// byte offset of token t (t a multiple of 2) in V^T row `row`: 4-token groups
+// are permuted by an XOR with (row >> 3) & 15, so the staging writes of one
+// token group to rows 8c + e spread over the banks (t & 3 stays in place)
+__device__ __forceinline__ int vt_col(int row, int t) {
+  return 2 * ((((t >> 2) ^ (row >> 3)) & 15) * 4 + (t & 3));
+}
+
+// two fp32 -> packed bf16 (round to nearest even) on the hardware converter
+__device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
+template <int D, int HB, int RB>
 __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p) {
   constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension
   constexpr int DB = D / 16;                 // 16-dim blocks of the output
   constexpr int CPT = D / 8;                 // 16-byte chunks per token row
-  constexpr int TPS = kThreads / CPT;        // tokens staged per pass
-  constexpr int PASSES = kKT / TPS;
-  constexpr int TCH = 4 / HB;                // 16-row chunks per workgroup
+  constexpr int TQ = kKT * CPT / kThreads;   // consecutive tokens staged per thread
+  static_assert(TQ == 2 || TQ == 4, "staging layout");
+  constexpr int R = 16 * RB;                 // query rows per wave (RB blocks of 16)
+  constexpr int WPH = 4 / HB;                // waves per q head
+  constexpr int RW = WPH * R;                // query rows per workgroup and head
+  constexpr int CH = kQTile / RW;            // workgroups along one host tile
+  static_assert(CH * RW == kQTile, "row split");
   constexpr int KPITCH = D * 2 + 16;         // bytes per K row in LDS (padded)
   constexpr int VPITCH = kKT * 2 + 16;       // bytes per V^T row (one dimension) in LDS
   __shared__ __attribute__((aligned(16))) unsigned char sm_k[kKT * KPITCH];
@@ -58,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int host_tile = blockIdx.x / HB, chunk = blockIdx.x % HB;
+  const int host_tile = blockIdx.x / CH, chunk = blockIdx.x % CH;
   const int hgroups = (p.G + HB - 1) / HB;
   const int g = blockIdx.y / hgroups, hg = blockIdx.y % hgroups;
   const int b = p.tile_to_batch[host_tile];
@@ -68,18 +87,22 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
   const int q_len = min(p.qo_indptr[b + 1], p.total_q) - q0;
   const int kv_len = min(max(p.kv_lens[b], 0), p.max_pages << p.page_log2);
   // rows of this workgroup within the request, and of this wave
-  const int wg_row0 = p.tile_to_index[host_tile] * kQTile + chunk * (kQTile / HB);
-  const int wg_rows = min(kQTile / HB, q_len - wg_row0);
+  const int wg_row0 = p.tile_to_index[host_tile] * kQTile + chunk * RW;
+  const int wg_rows = min(RW, q_len - wg_row0);
   if (wg_row0 < 0 || wg_rows <= 0) return;                   // whole workgroup
-  const int head_slot = wave / TCH;
-  const int h_in_group = hg * HB + head_slot;
+  const int h_in_group = hg * HB + wave / WPH;
   const bool head_ok = h_in_group < p.G;
   const int h = g * p.G + (head_ok ? h_in_group : 0);
-  const int row0 = wg_row0 + (wave % TCH) * 16;              // first row of this wave
-  const int my_row = row0 + (lane & 15);                      // this lane's query row
-  const bool row_ok = head_ok && my_row < q_len;
+  const int row0 = wg_row0 + (wave % WPH) * R;               // first row of this wave
   const int pos_base = kv_len - q_len;                        // position of row 0
-  const int my_pos = pos_base + my_row;
+  int my_row[RB], my_pos[RB];
+  bool row_ok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    my_row[rb] = row0 + 16 * rb + (lane & 15);                // this lane's query rows
+    row_ok[rb] = head_ok && my_row[rb] < q_len;
+    my_pos[rb] = pos_base + my_row[rb];
+  }
   // positions the workgroup needs: [0, kv_end)
   const int kv_end = p.causal ? min(kv_len, pos_base + wg_row0 + wg_rows) : kv_len;
   const int log2P = p.page_log2, pmask = (1 << log2P) - 1;
@@ -87,53 +110,74 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
   const size_t row_stride = size_t(p.Hkv) * D;
 
   // Q^T as the B operand: lane = query row (lane & 15), dims 32j + 8(lane >> 4)
-  bf16x8 qb[KS];
+  bf16x8 qb[RB][KS];
 #pragma unroll
-  for (int j = 0; j < KS; ++j) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (row_ok) w = *reinterpret_cast<const u32x4 *>(p.q + (size_t(q0 + my_row) * p.Hq + h) * D + 32 * j + 8 * (lane >> 4));
-    qb[j] = as_bf16x8(w);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (row_ok[rb])
+        w = *reinterpret_cast<const u32x4 *>(p.q + (size_t(q0 + my_row[rb]) * p.Hq + h) * D + 32 * j + 8 * (lane >> 4));
+      qb[rb][j] = as_bf16x8(w);
+    }
+
+  float m[RB], l[RB];   // running max (log2 domain) and this lane's partial sum, per row block
+  f32x4 o[RB][DB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  float m = -INFINITY, l = 0.f;   // running max (log2 domain) and this lane's partial sum
-  f32x4 o[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // staging: thread -> (token tok0 + TPS * pass, 16-byte chunk c)
-  const int c = threadIdx.x % CPT, tok0 = threadIdx.x / CPT;
-  u32x4 kreg[PASSES], vreg[PASSES];
+  // staging: thread -> TQ consecutive tokens tq0 .. tq0+TQ-1 of one 16-byte chunk c,
+  // so V^T is written TQ tokens (2*TQ bytes) at a time for each of its 8 dims
+  const int c = threadIdx.x % CPT, tq0 = (threadIdx.x / CPT) * TQ;
+  u32x4 kreg[TQ], vreg[TQ];
   auto load_tile = [&](int t0) {
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int t = t0 + tok0 + TPS * ps;
-      kreg[ps] = u32x4{0u, 0u, 0u, 0u};
-      vreg[ps] = u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < TQ; ++k) {
+      const int t = t0 + tq0 + k;
+      kreg[k] = u32x4{0u, 0u, 0u, 0u};
+      vreg[k] = u32x4{0u, 0u, 0u, 0u};
       if (t < kv_end) {
         const int raw = pt[t >> log2P];
         const int pid = unsigned(raw) < unsigned(p.num_pages) ? raw : 0;
         const size_t row = (size_t(pid) << log2P) + (t & pmask);
         const size_t off = row * row_stride + size_t(g) * D + 8 * c;
-        kreg[ps] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k_pool + off));
-        vreg[ps] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.v_pool + off));
+        kreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k_pool + off));
+        vreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.v_pool + off));
         if (unsigned(raw) >= unsigned(p.num_pages)) {   // a bad page id poisons the row
-          kreg[ps] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-          vreg[ps] = kreg[ps];
+          kreg[k] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+          vreg[k] = kreg[k];
         }
       }
     }
   };
   auto stage_tile = [&]() {
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int tt = tok0 + TPS * ps;
-      *reinterpret_cast<u32x4 *>(sm_k + tt * KPITCH + 16 * c) = kreg[ps];
-      // V^T: dimension 8c + e, token tt
+    for (int k = 0; k < TQ; ++k)
+      *reinterpret_cast<u32x4 *>(sm_k + (tq0 + k) * KPITCH + 16 * c) = kreg[k];
+    // V^T row (dimension) 8c + e gets the TQ tokens' values of that dimension.
+    // 4-token groups are permuted within a row (vt_col): without it
+    // the 16 lanes writing rows 8c + e of one token group hit 2 banks.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned w = vreg[ps][e];
-        *reinterpret_cast<uint16_t *>(sm_vt + (8 * c + 2 * e) * VPITCH + 2 * tt) = uint16_t(w & 0xffffu);
-        *reinterpret_cast<uint16_t *>(sm_vt + (8 * c + 2 * e + 1) * VPITCH + 2 * tt) = uint16_t(w >> 16);
+    for (int e = 0; e < 8; ++e) {
+      uint16_t v[TQ];
+#pragma unroll
+      for (int k = 0; k < TQ; ++k) {
+        const unsigned w = vreg[k][e >> 1];
+        v[k] = uint16_t((e & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+      unsigned char *dst = sm_vt + (8 * c + e) * VPITCH + vt_col(8 * c + e, tq0);
+      if constexpr (TQ == 4) {
+        u32x2 pk;
+        pk[0] = unsigned(v[0]) | (unsigned(v[1]) << 16);
+        pk[1] = unsigned(v[2]) | (unsigned(v[3]) << 16);
+        *reinterpret_cast<u32x2 *>(dst) = pk;
+      } else {
+        *reinterpret_cast<unsigned *>(dst) = unsigned(v[0]) | (unsigned(v[1]) << 16);
       }
     }
   };
@@ -146,100 +190,133 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
     __syncthreads();
     if (kt + 1 < ntiles) load_tile((kt + 1) * kKT);   // in flight while this tile is computed
     const int t0 = kt * kKT;
+    // every position of the tile is seen by every row of the workgroup: no mask
+    const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= pos_base + wg_row0);
 
-    // S^T for 4 blocks of 16 tokens: lane holds tokens 16mb + 4(lane >> 4) + r of row lane & 15
-    f32x4 s[4];
+    // S^T for 4 blocks of 16 tokens: lane holds tokens 16mb + 4(lane >> 4) + r of
+    // row (lane & 15) of each row block; one K read from LDS feeds RB products
+    f32x4 s[RB][4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         const u32x4 ka = *reinterpret_cast<const u32x4 *>(sm_k + (16 * mb + (lane & 15)) * KPITCH + 2 * (32 * j + 8 * (lane >> 4)));
-        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          s[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[rb][j], s[rb][mb], 0, 0, 0);
       }
     }
-    // scale (log2 domain), mask, tile max of this lane's row
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = t0 + 16 * mb + 4 * (lane >> 4) + r;
-        const bool seen = pos < kv_end && (!p.causal || pos <= my_pos);
-        const float x = seen ? s[mb][r] * p.scale_log2 : -INFINITY;
-        s[mb][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mn = fmaxf(m, tmax);
-    const float alpha = (m == mn) ? 1.f : fast_exp2(m - mn);
-    m = mn;
-    l *= alpha;
     // probabilities in the B layout of P^T: k-slot 8(lane >> 4) + i <-> token
     // 32kb + 4(lane >> 4) + i (i < 4) or 32kb + 16 + 4(lane >> 4) + i - 4
-    u32x4 pb[2];
+    u32x4 pb[RB][2];
+    float alpha[RB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      // scale (log2 domain), mask, tile max of this lane's row
+      float tmax = -INFINITY;
+      if (full_tile) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          const float x0 = s[2 * kb + half][r], x1 = s[2 * kb + half][r + 1];
-          const float p0 = mn == -INFINITY ? 0.f : fast_exp2(x0 - mn);
-          const float p1 = mn == -INFINITY ? 0.f : fast_exp2(x1 - mn);
-          l += p0 + p1;
-          pb[kb][2 * half + r / 2] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const float x = s[rb][mb][r] * p.scale_log2;
+            s[rb][mb][r] = x;
+            tmax = fmaxf(tmax, x);
+          }
+      } else {
 #pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] *= alpha;
-    // O^T += V^T P^T over the tile's two 32-token k-blocks
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int pos = t0 + 16 * mb + 4 * (lane >> 4) + r;
+            const bool seen = pos < kv_end && (!p.causal || pos <= my_pos[rb]);
+            const float x = seen ? s[rb][mb][r] * p.scale_log2 : -INFINITY;
+            s[rb][mb][r] = x;
+            tmax = fmaxf(tmax, x);
+          }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mn = fmaxf(m[rb], tmax);
+      alpha[rb] = (m[rb] == mn) ? 1.f : fast_exp2(m[rb] - mn);
+      m[rb] = mn;
+      l[rb] *= alpha[rb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const float x0 = s[rb][2 * kb + half][r], x1 = s[rb][2 * kb + half][r + 1];
+            const float p0 = mn == -INFINITY ? 0.f : fast_exp2(x0 - mn);
+            const float p1 = mn == -INFINITY ? 0.f : fast_exp2(x1 - mn);
+            l[rb] += p0 + p1;
+            pb[rb][kb][2 * half + r / 2] = cvt_pk_bf16(p0, p1);
+          }
+#pragma unroll
+      for (int i = 0; i < DB; ++i) o[rb][i] *= alpha[rb];
+    }
+    // O^T += V^T P^T over the tile's two 32-token k-blocks; one V^T read feeds RB products
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int i = 0; i < DB; ++i) {
-        const unsigned char *vrow = sm_vt + (16 * i + (lane & 15)) * VPITCH;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 2 * (32 * kb + 4 * (lane >> 4)));
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 2 * (32 * kb + 16 + 4 * (lane >> 4)));
+        const int vr = 16 * i + (lane & 15);
+        const unsigned char *vrow = sm_vt + vr * VPITCH;
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + vt_col(vr, 32 * kb + 4 * (lane >> 4)));
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + vt_col(vr, 32 * kb + 16 + 4 * (lane >> 4)));
         const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-        o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb[kb]), o[i], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb[rb][kb]), o[rb][i], 0, 0, 0);
       }
     }
   }
 
   // row sums over the 4 lane groups, then the output rows
-  float lsum = l;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (!row_ok) return;
-  const float inv = 1.f / lsum;
-  uint16_t *orow = p.out + (size_t(q0 + my_row) * p.Hq + h) * D;
 #pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    u32x2 w;
-    w[0] = f32_to_bf16_rne(o[i][0] * inv) | (f32_to_bf16_rne(o[i][1] * inv) << 16);
-    w[1] = f32_to_bf16_rne(o[i][2] * inv) | (f32_to_bf16_rne(o[i][3] * inv) << 16);
-    *reinterpret_cast<u32x2 *>(orow + 16 * i + 4 * (lane >> 4)) = w;
+  for (int rb = 0; rb < RB; ++rb) {
+    float lsum = l[rb];
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (!row_ok[rb]) continue;
+    const float inv = 1.f / lsum;
+    uint16_t *orow = p.out + (size_t(q0 + my_row[rb]) * p.Hq + h) * D;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      u32x2 w;
+      w[0] = f32_to_bf16_rne(o[rb][i][0] * inv) | (f32_to_bf16_rne(o[rb][i][1] * inv) << 16);
+      w[1] = f32_to_bf16_rne(o[rb][i][2] * inv) | (f32_to_bf16_rne(o[rb][i][3] * inv) << 16);
+      *reinterpret_cast<u32x2 *>(orow + 16 * i + 4 * (lane >> 4)) = w;
+    }
+    if (p.lse && lane < 16)
+      p.lse[size_t(q0 + my_row[rb]) * p.Hq + h] = (m[rb] + __builtin_amdgcn_logf(lsum)) * kLn2;
   }
-  if (p.lse && lane < 16) p.lse[size_t(q0 + my_row) * p.Hq + h] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
-template <int D, int HB>
+template <int D, int HB, int RB>
 hipError_t launch(const PrefillParams &p, hipStream_t stream) {
+  constexpr int CH = kQTile / ((4 / HB) * 16 * RB);
   const int hgroups = (p.G + HB - 1) / HB;
-  const dim3 grid{unsigned(p.num_q_tiles * HB), unsigned(p.Hkv * hgroups)}, block{kThreads};
-  hipLaunchKernelGGL((paged_prefill_kernel<D, HB>), grid, block, 0, stream, p);
+  const dim3 grid{unsigned(p.num_q_tiles * CH), unsigned(p.Hkv * hgroups)}, block{kThreads};
+  hipLaunchKernelGGL((paged_prefill_kernel<D, HB, RB>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_paged_prefill(const PrefillParams &p, hipStream_t stream) {
+  // HB = min(G, 4) q heads per workgroup.  At D = 64 a wave takes two 16-row
+  // blocks once a workgroup holds two or more heads (one K/V^T read from LDS
+  // then feeds two products); at D = 128 the second block's registers would
+  // leave one wave per SIMD, which measured slower, so a wave keeps one block.
   const int HB = p.G < 4 ? p.G : 4;
-#define PKV_CASE(DD, HH) \
-  if (p.D == DD && HB == HH) return launch<DD, HH>(p, stream);
-  PKV_CASE(64, 1) PKV_CASE(64, 2) PKV_CASE(64, 4)
-  PKV_CASE(128, 1) PKV_CASE(128, 2) PKV_CASE(128, 4)
+#define PKV_CASE(DD, HH, RR) \
+  if (p.D == DD && HB == HH) return launch<DD, HH, RR>(p, stream);
+  PKV_CASE(64, 1, 1) PKV_CASE(64, 2, 2) PKV_CASE(64, 4, 2)
+  PKV_CASE(128, 1, 1) PKV_CASE(128, 2, 1) PKV_CASE(128, 4, 1)
 #undef PKV_CASE
   return hipErrorInvalidValue;
 }
