@@ -8,6 +8,7 @@
 
 #include "pkv.h"
 #include "pkv_launch.h"
+#include "pkv_prefill_launch.h"
 
 namespace {
 

@@ -29,6 +29,7 @@
 #include "pkv.h"
 #include "pkv_device.h"
 #include "pkv_launch.h"
+#include "pkv_prefill_launch.h"
 
 namespace pkv {
 namespace {
