@@ -11,6 +11,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -21,11 +22,16 @@ SOURCES = ["pkv_api.hip", "pkv_store.hip", "pkv_decode.hip", "pkv_decode_mfma.hi
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
     f"-I{ROOT / 'include'}", f"-I{CSRC}",
 ]
+# Per-source extras.  The prefill kernel keeps its matrix-core accumulators
+# in ordinary VGPRs (the accumulator-register form costs a copy in and out of
+# every rescaled accumulator each K/V tile).
+SOURCE_FLAGS = {"pkv_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -34,18 +40,36 @@ def hipcc() -> str:
     return str(cand) if cand.exists() else "hipcc"
 
 
+def _run(procs, verbose):
+    errs = []
+    for cmd, pr in procs:
+        out, err = pr.communicate()
+        err = "\n".join(line for line in err.splitlines() if NOISE not in line)
+        if pr.returncode != 0:
+            errs.append(f"hipcc failed ({pr.returncode}): {' '.join(cmd)}\n{err}")
+        elif err.strip() and verbose:
+            print(err, file=sys.stderr)
+    if errs:
+        raise RuntimeError("\n".join(errs))
+
+
 def build(verbose: bool = False) -> Path:
+    """Compile every source to an object (in parallel), then link libpkv.so."""
     tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
-    cmd = [hipcc(), *HIPCC_FLAGS, *[str(CSRC / s) for s in SOURCES], "-o", str(tmp)]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(line for line in r.stderr.splitlines() if noise not in line)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    with tempfile.TemporaryDirectory(prefix="pkv_build_") as objdir:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = str(Path(objdir) / (Path(src).stem + ".o"))
+            cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", str(CSRC / src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        _run(procs, verbose)
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", str(tmp)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        _run([(cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))], verbose)
     os.replace(tmp, LIB)
     return LIB
 

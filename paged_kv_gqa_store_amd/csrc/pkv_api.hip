@@ -282,7 +282,9 @@ pkv_status pkv_paged_prefill_attn(const void *q, const void *k_pool, const void 
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size > 1024) return PKV_ERR_UNSUPPORTED;
-  if (B > 65535 || Hkv > 65535 || int64_t(num_q_tiles) * 4 > int64_t(INT32_MAX)) return PKV_ERR_SHAPE;
+  // one workgroup per (q tile, row chunk <= 4, kv head, head half <= 2)
+  if (B > 65535 || Hkv > 65535 || int64_t(num_q_tiles) * 4 * Hkv * 2 > int64_t(INT32_MAX))
+    return PKV_ERR_SHAPE;
   if (int64_t(num_pages) * page_size > (int64_t(1) << 31)) return PKV_ERR_SHAPE;
   if (int64_t(max_pages_per_seq) * page_size > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
   if (!(scale > 0.f) || !isfinite(scale)) return PKV_ERR_SHAPE;

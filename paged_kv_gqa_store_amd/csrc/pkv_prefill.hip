@@ -78,9 +78,19 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int host_tile = blockIdx.x / CH, chunk = blockIdx.x % CH;
+  // 1-D grid, XCD-aware: consecutive workgroup ids go round-robin to the 8
+  // XCDs, so id i is given logical slot (i % 8) * (n / 8) + i / 8 and each XCD
+  // runs a contiguous slice of the logical order (kv-head group major, then
+  // q chunks), whose workgroups read the same K/V rows through one L2.  The
+  // q chunks run last-first: with the causal mask they are the longest.
   const int hgroups = (p.G + HB - 1) / HB;
-  const int g = blockIdx.y / hgroups, hg = blockIdx.y % hgroups;
+  const int n_x = p.num_q_tiles * CH;                         // workgroups per group
+  const unsigned nwg = gridDim.x, per_xcd = nwg / 8;
+  const unsigned lin = blockIdx.x;
+  const int logical = int(lin < 8 * per_xcd ? (lin % 8) * per_xcd + lin / 8 : lin);
+  const int gy = logical / n_x, qx = n_x - 1 - logical % n_x;
+  const int host_tile = qx / CH, chunk = qx % CH;
+  const int g = gy / hgroups, hg = gy % hgroups;
   const int b = p.tile_to_batch[host_tile];
   if (unsigned(b) >= unsigned(p.B)) return;                   // whole workgroup
   // rows past total_q and positions past the page table are never touched
@@ -183,13 +193,49 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
     }
   };
 
+  // Fast path: with pages of at least TQ tokens a thread's TQ tokens share one
+  // page, so it needs one page-table entry per tile, fetched a tile ahead.
+  // It is taken when no page id the workgroup reads is out of the pool (one
+  // scan up front); otherwise every token is looked up and checked.
+  const int npg = (kv_end + pmask) >> log2P;
+  int bad_ids = 0;
+  for (int i = threadIdx.x; i < npg; i += kThreads) bad_ids |= unsigned(pt[i]) >= unsigned(p.num_pages);
+  const bool fast = __builtin_amdgcn_readfirstlane(__syncthreads_or(bad_ids)) == 0 && (1 << log2P) >= TQ;
+  auto page_of = [&](int t) { return t < kv_end ? pt[t >> log2P] : 0; };
+  auto load_tile_fast = [&](int t0, int pid) {
+    const int tt = t0 + tq0;
+    const size_t off = ((size_t(pid) << log2P) + (tt & pmask)) * row_stride + size_t(g) * D + 8 * c;
+#pragma unroll
+    for (int k = 0; k < TQ; ++k) {
+      kreg[k] = u32x4{0u, 0u, 0u, 0u};
+      vreg[k] = u32x4{0u, 0u, 0u, 0u};
+      if (tt + k < kv_end) {
+        kreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k_pool + off + k * row_stride));
+        vreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.v_pool + off + k * row_stride));
+      }
+    }
+  };
+
   const int ntiles = (kv_end + kKT - 1) / kKT;
-  load_tile(0);
+  int pid_next = 0;
+  if (fast) {
+    load_tile_fast(0, page_of(tq0));
+    pid_next = page_of(kKT + tq0);
+  } else {
+    load_tile(0);
+  }
   for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();                 // the previous tile's LDS reads are done
     stage_tile();
     __syncthreads();
-    if (kt + 1 < ntiles) load_tile((kt + 1) * kKT);   // in flight while this tile is computed
+    if (kt + 1 < ntiles) {           // in flight while this tile is computed
+      if (fast) {
+        load_tile_fast((kt + 1) * kKT, pid_next);
+        pid_next = page_of((kt + 2) * kKT + tq0);
+      } else {
+        load_tile((kt + 1) * kKT);
+      }
+    }
     const int t0 = kt * kKT;
     // every position of the tile is seen by every row of the workgroup: no mask
     const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= pos_base + wg_row0);
@@ -210,22 +256,23 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
       }
     }
     // probabilities in the B layout of P^T: k-slot 8(lane >> 4) + i <-> token
-    // 32kb + 4(lane >> 4) + i (i < 4) or 32kb + 16 + 4(lane >> 4) + i - 4
-    u32x4 pb[RB][2];
-    float alpha[RB];
+    // 32kb + 4(lane >> 4) + i (i < 4) or 32kb + 16 + 4(lane >> 4) + i - 4.
+    // The running max m (log2 domain) moves only when a row's tile max passes
+    // it by more than kLazy: until then the probabilities are taken against
+    // the old max (at most 2^kLazy, exact in fp32 and bf16 range) and the
+    // accumulators need no rescale; o / l is the same quotient either way.
+    constexpr float kLazy = 8.f;
+    float ts[RB];
+    bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // scale (log2 domain), mask, tile max of this lane's row
+      // mask, then the tile max of this lane's row on the raw scores (scale > 0)
       float tmax = -INFINITY;
       if (full_tile) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float x = s[rb][mb][r] * p.scale_log2;
-            s[rb][mb][r] = x;
-            tmax = fmaxf(tmax, x);
-          }
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[rb][mb][r]);
       } else {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
@@ -233,31 +280,41 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
           for (int r = 0; r < 4; ++r) {
             const int pos = t0 + 16 * mb + 4 * (lane >> 4) + r;
             const bool seen = pos < kv_end && (!p.causal || pos <= my_pos[rb]);
-            const float x = seen ? s[rb][mb][r] * p.scale_log2 : -INFINITY;
-            s[rb][mb][r] = x;
-            tmax = fmaxf(tmax, x);
+            s[rb][mb][r] = seen ? s[rb][mb][r] : -INFINITY;
+            tmax = fmaxf(tmax, s[rb][mb][r]);
           }
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m[rb], tmax);
-      alpha[rb] = (m[rb] == mn) ? 1.f : fast_exp2(m[rb] - mn);
-      m[rb] = mn;
-      l[rb] *= alpha[rb];
+      ts[rb] = tmax * p.scale_log2;
+      grow |= ts[rb] > m[rb] + kLazy;
+    }
+    if (__any(grow)) {               // wave-uniform: rescale every row block
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mn = fmaxf(m[rb], ts[rb]);
+        const float alpha = (m[rb] == mn) ? 1.f : fast_exp2(m[rb] - mn);
+        m[rb] = mn;
+        l[rb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[rb][i] *= alpha;
+      }
+    }
+    u32x4 pb[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float nm = m[rb] == -INFINITY ? 0.f : -m[rb];   // masked scores give exp2(-inf) = 0
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int r = 0; r < 4; r += 2) {
-            const float x0 = s[rb][2 * kb + half][r], x1 = s[rb][2 * kb + half][r + 1];
-            const float p0 = mn == -INFINITY ? 0.f : fast_exp2(x0 - mn);
-            const float p1 = mn == -INFINITY ? 0.f : fast_exp2(x1 - mn);
+            const float p0 = fast_exp2(fmaf(s[rb][2 * kb + half][r], p.scale_log2, nm));
+            const float p1 = fast_exp2(fmaf(s[rb][2 * kb + half][r + 1], p.scale_log2, nm));
             l[rb] += p0 + p1;
             pb[rb][kb][2 * half + r / 2] = cvt_pk_bf16(p0, p1);
           }
-#pragma unroll
-      for (int i = 0; i < DB; ++i) o[rb][i] *= alpha[rb];
     }
     // O^T += V^T P^T over the tile's two 32-token k-blocks; one V^T read feeds RB products
 #pragma unroll
@@ -301,7 +358,7 @@ template <int D, int HB, int RB>
 hipError_t launch(const PrefillParams &p, hipStream_t stream) {
   constexpr int CH = kQTile / ((4 / HB) * 16 * RB);
   const int hgroups = (p.G + HB - 1) / HB;
-  const dim3 grid{unsigned(p.num_q_tiles * CH), unsigned(p.Hkv * hgroups)}, block{kThreads};
+  const dim3 grid{unsigned(p.num_q_tiles * CH * p.Hkv * hgroups)}, block{kThreads};
   hipLaunchKernelGGL((paged_prefill_kernel<D, HB, RB>), grid, block, 0, stream, p);
   return hipGetLastError();
 }

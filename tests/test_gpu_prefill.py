@@ -115,6 +115,45 @@ def test_bad_page_poisons_its_request_only(gpu_device):
     assert torch.isfinite(out[:qo[1]]).all() and torch.isfinite(out[qo[2]:]).all()
 
 
+@pytest.mark.parametrize("rate", [0.006, 0.05])
+def test_scores_growing_along_positions(gpu_device, rate):
+    """Keys aligned with their group's queries and growing along the positions
+    make every row's running max climb from tile to tile: slowly (a few
+    binades per 64 positions, so probabilities above 1 against an older max)
+    or fast (the max moves on every tile)."""
+    Hkv, G, D, P = 2, 4, 128, 16
+    q_lens, kv_lens = (40, 200, 1), (300, 700, 129)
+    cfg = W.PrefillConfig(0, f"growing{rate}", G * Hkv, Hkv, D, P,
+                          -(-sum(kv_lens) // P) + len(kv_lens) + 4, q_lens, kv_lens)
+    q, kp, vp, pt, kl, qo = W.make_prefill_inputs(cfg)
+    as_f32 = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
+    rng = np.random.Generator(np.random.PCG64(31))
+    u = rng.standard_normal((Hkv, D)).astype(np.float32)
+    qf = 0.3 * as_f32(q) + np.repeat(u, G, axis=0)[None]
+    kf = as_f32(kp)
+    for b in range(len(kv_lens)):
+        t = np.arange(kv_lens[b])
+        pages, slots = pt[b, t // P], t % P
+        kf[pages, slots] = 0.3 * kf[pages, slots] + rate * t[:, None, None] * u[None]
+    q, kp = W.to_bf16_bits(qf), W.to_bf16_bits(kf)
+    for causal in (True, False):
+        out, lse = run(q, kp, vp, pt, kl, qo, gpu_device, causal)
+        ref, ref_lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, causal)
+        check_attention(out, ref, f"prefill growing scores rate={rate} causal={causal}")
+        check_lse(lse, ref_lse)
+
+
+def test_page_table_entries_past_the_sequence_are_not_read(gpu_device):
+    cfg = W.PREFILL["ragged_chunks"]
+    q, kp, vp, pt, kl, qo = W.make_prefill_inputs(cfg)
+    a = run(q, kp, vp, pt, kl, qo, gpu_device, True, want_lse=False)
+    pt = pt.copy()
+    for b in range(cfg.B):
+        pt[b, -(-int(kl[b]) // cfg.P):] = -7          # out of the pool, but unused
+    c = run(q, kp, vp, pt, kl, qo, gpu_device, True, want_lse=False)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
 def test_prefill_errors(gpu_device):
     cfg = W.PREFILL["ragged_chunks"]
     q, kp, vp, pt, kl, qo = W.make_prefill_inputs(cfg)
