@@ -18,12 +18,17 @@
 //                  tokens per register group, so the online softmax of a row
 //                  reduces over 16 registers and the 4 lane groups.
 //   O^T += V^T P^T the probabilities are already in the B-operand layout of
-//                  P^T (8 tokens of the lane's row); A = V^T is read from a
-//                  transposed V tile that the workgroup writes into LDS while
-//                  staging it.  P is rounded to bf16 for the matrix core;
-//                  the accumulators and the softmax statistics stay fp32.
-// The workgroup's 4 waves share each 64-token K/V tile; the next tile's
-// global loads are in flight while the current one is computed.
+//                  P^T (8 tokens of the lane's row); A = V^T comes straight
+//                  from the row-major V tile through the LDS transpose read
+//                  (ds_read_b64_tr_b16).  P is rounded to bf16 for the matrix
+//                  core; the accumulators and the softmax statistics stay fp32.
+// K and V tiles of 64 tokens move from the pool into LDS with direct loads
+// (global_load_lds_dwordx4: 16 bytes per lane, no registers, no staging
+// code), double-buffered, so one barrier per tile separates the loads of tile
+// t + 1 from the reads of tile t.  Each row's 16-byte chunks are permuted by
+// an XOR with a function of the row (swz below) chosen so that both the K
+// reads (16 rows, one chunk) and the transpose reads (4 rows, 2 chunks per
+// 16-lane group) hit distinct banks.
 #include <math.h>
 
 #include "pkv.h"
@@ -38,19 +43,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQTile = PKV_PREFILL_TILE_ROWS;   // query rows per host tile
 constexpr int kKT = 64;                         // tokens per K/V tile
 constexpr int kThreads = 256;                   // 4 waves
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
-
-// byte offset of token t (t a multiple of 2) in V^T row `row`: 4-token groups
-// are permuted by an XOR with (row >> 3) & 15, so the staging writes of one
-// token group to rows 8c + e spread over the banks (t & 3 stays in place)
-__device__ __forceinline__ int vt_col(int row, int t) {
-  return 2 * ((((t >> 2) ^ (row >> 3)) & 15) * 4 + (t & 3));
-}
 
 // two fp32 -> packed bf16 (round to nearest even) on the hardware converter
 __device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
@@ -59,22 +58,46 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// 16-byte chunk permutation of K/V row r (only r & 15 matters): an XOR with a
+// bit shuffle of r such that chunk c of 16 consecutive rows lands on distinct
+// chunks, and so do chunks {2i, 2i + 1} of rows 4a .. 4a + 3 (D = 128: 16
+// chunks per 256-byte row; D = 64: 8 chunks per 128-byte row, where rows of
+// one parity also share banks).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  if constexpr (D == 128) return r2 | (r0 << 1) | (r1 << 2) | (r3 << 3);
+  else return r2 | ((r0 ^ r3) << 1) | ((r1 ^ r2) << 2);
+}
+
+// 16-byte sources for direct loads of rows that are not in the pool: zeros
+// past the sequence end (masked positions must not carry NaN into P V), NaN
+// for a page id outside the pool
+__device__ __attribute__((aligned(16))) u32x4 kFillRows[2] = {
+    {0u, 0u, 0u, 0u}, {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}};
+
+#define PKV_LDS __attribute__((address_space(3)))
+
 template <int D, int HB, int RB>
 __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p) {
   constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension
   constexpr int DB = D / 16;                 // 16-dim blocks of the output
-  constexpr int CPT = D / 8;                 // 16-byte chunks per token row
-  constexpr int TQ = kKT * CPT / kThreads;   // consecutive tokens staged per thread
-  static_assert(TQ == 2 || TQ == 4, "staging layout");
+  constexpr int PITCH = 2 * D;               // bytes per K/V row in LDS
+  constexpr int LPR = D / 8;                 // lanes (16-byte chunks) per row
+  constexpr int RPI = 64 / LPR;              // rows per direct load (64 lanes)
+  constexpr int NI = kKT / (4 * RPI);        // direct loads per wave, tile and tensor
   constexpr int R = 16 * RB;                 // query rows per wave (RB blocks of 16)
   constexpr int WPH = 4 / HB;                // waves per q head
   constexpr int RW = WPH * R;                // query rows per workgroup and head
   constexpr int CH = kQTile / RW;            // workgroups along one host tile
   static_assert(CH * RW == kQTile, "row split");
-  constexpr int KPITCH = D * 2 + 16;         // bytes per K row in LDS (padded)
-  constexpr int VPITCH = kKT * 2 + 16;       // bytes per V^T row (one dimension) in LDS
-  __shared__ __attribute__((aligned(16))) unsigned char sm_k[kKT * KPITCH];
-  __shared__ __attribute__((aligned(16))) unsigned char sm_vt[D * VPITCH];
+  static_assert(16 % RPI == 0 || RPI == 16, "a wave loads whole 16-row groups");
+  // two buffers per tensor, separate objects so that reads of one buffer
+  // need not wait for the direct loads in flight into the other
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k0[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v0[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k1[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v1[kKT * PITCH];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -142,101 +165,50 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
     for (int i = 0; i < DB; ++i) o[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // staging: thread -> TQ consecutive tokens tq0 .. tq0+TQ-1 of one 16-byte chunk c,
-  // so V^T is written TQ tokens (2*TQ bytes) at a time for each of its 8 dims
-  const int c = threadIdx.x % CPT, tq0 = (threadIdx.x / CPT) * TQ;
-  u32x4 kreg[TQ], vreg[TQ];
-  auto load_tile = [&](int t0) {
+  // Direct loads: load n of this wave fills tile rows 16 * wave + n * RPI + lrow
+  // (lrow = lane / LPR); the lane's 16 bytes land at physical chunk lane % LPR,
+  // so it fetches the logical chunk that swz maps there.
+  const int lrow = lane / LPR, pc = lane % LPR;
+  int pid[NI];                       // page ids of this lane's rows in the next tile to load
+  auto fetch_pids = [&](int t0) {
 #pragma unroll
-    for (int k = 0; k < TQ; ++k) {
-      const int t = t0 + tq0 + k;
-      kreg[k] = u32x4{0u, 0u, 0u, 0u};
-      vreg[k] = u32x4{0u, 0u, 0u, 0u};
-      if (t < kv_end) {
-        const int raw = pt[t >> log2P];
-        const int pid = unsigned(raw) < unsigned(p.num_pages) ? raw : 0;
-        const size_t row = (size_t(pid) << log2P) + (t & pmask);
-        const size_t off = row * row_stride + size_t(g) * D + 8 * c;
-        kreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k_pool + off));
-        vreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.v_pool + off));
-        if (unsigned(raw) >= unsigned(p.num_pages)) {   // a bad page id poisons the row
-          kreg[k] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-          vreg[k] = kreg[k];
-        }
-      }
+    for (int n = 0; n < NI; ++n) {
+      const int t = t0 + 16 * wave + n * RPI + lrow;
+      pid[n] = t < kv_end ? pt[t >> log2P] : 0;
     }
   };
-  auto stage_tile = [&]() {
+  const u32x4 *fill = kFillRows;
+  auto issue = [&](int t0, unsigned char *kb, unsigned char *vb) {
 #pragma unroll
-    for (int k = 0; k < TQ; ++k)
-      *reinterpret_cast<u32x4 *>(sm_k + (tq0 + k) * KPITCH + 16 * c) = kreg[k];
-    // V^T row (dimension) 8c + e gets the TQ tokens' values of that dimension.
-    // 4-token groups are permuted within a row (vt_col): without it
-    // the 16 lanes writing rows 8c + e of one token group hit 2 banks.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t v[TQ];
-#pragma unroll
-      for (int k = 0; k < TQ; ++k) {
-        const unsigned w = vreg[k][e >> 1];
-        v[k] = uint16_t((e & 1) ? (w >> 16) : (w & 0xffffu));
-      }
-      unsigned char *dst = sm_vt + (8 * c + e) * VPITCH + vt_col(8 * c + e, tq0);
-      if constexpr (TQ == 4) {
-        u32x2 pk;
-        pk[0] = unsigned(v[0]) | (unsigned(v[1]) << 16);
-        pk[1] = unsigned(v[2]) | (unsigned(v[3]) << 16);
-        *reinterpret_cast<u32x2 *>(dst) = pk;
-      } else {
-        *reinterpret_cast<unsigned *>(dst) = unsigned(v[0]) | (unsigned(v[1]) << 16);
-      }
+    for (int n = 0; n < NI; ++n) {
+      const int t = t0 + 16 * wave + n * RPI + lrow;
+      const int c = pc ^ swz<D>(n * RPI + lrow);
+      const bool in_pool = t < kv_end && unsigned(pid[n]) < unsigned(p.num_pages);
+      const size_t off = ((size_t(in_pool ? pid[n] : 0) << log2P) + (t & pmask)) * row_stride +
+                         size_t(g) * D + 8 * c;
+      const u32x4 *alt = fill + (t < kv_end ? 1 : 0);
+      const u32x4 *ks = in_pool ? reinterpret_cast<const u32x4 *>(p.k_pool + off) : alt;
+      const u32x4 *vs = in_pool ? reinterpret_cast<const u32x4 *>(p.v_pool + off) : alt;
+      const int dst = (16 * wave + n * RPI) * PITCH;
+      __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(ks), (PKV_LDS void *)(kb + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(vs), (PKV_LDS void *)(vb + dst), 16, 0, 0);
     }
   };
 
-  // Fast path: with pages of at least TQ tokens a thread's TQ tokens share one
-  // page, so it needs one page-table entry per tile, fetched a tile ahead.
-  // It is taken when no page id the workgroup reads is out of the pool (one
-  // scan up front); otherwise every token is looked up and checked.
-  const int npg = (kv_end + pmask) >> log2P;
-  int bad_ids = 0;
-  for (int i = threadIdx.x; i < npg; i += kThreads) bad_ids |= unsigned(pt[i]) >= unsigned(p.num_pages);
-  const bool fast = __builtin_amdgcn_readfirstlane(__syncthreads_or(bad_ids)) == 0 && (1 << log2P) >= TQ;
-  auto page_of = [&](int t) { return t < kv_end ? pt[t >> log2P] : 0; };
-  auto load_tile_fast = [&](int t0, int pid) {
-    const int tt = t0 + tq0;
-    const size_t off = ((size_t(pid) << log2P) + (tt & pmask)) * row_stride + size_t(g) * D + 8 * c;
+  // LDS read offsets.  K (A operand of S^T): row lane & 15 of a 16-row block,
+  // logical chunk 4j + (lane >> 4).  V (transpose read): lane 4k + q of
+  // 16-lane group G points at tile row 4G + k (+16), dims 16i + 4q .. + 3.
+  int koff[KS], voff[DB];
+  {
+    const int i = lane & 15, G = lane >> 4;
 #pragma unroll
-    for (int k = 0; k < TQ; ++k) {
-      kreg[k] = u32x4{0u, 0u, 0u, 0u};
-      vreg[k] = u32x4{0u, 0u, 0u, 0u};
-      if (tt + k < kv_end) {
-        kreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.k_pool + off + k * row_stride));
-        vreg[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p.v_pool + off + k * row_stride));
-      }
-    }
-  };
-
-  const int ntiles = (kv_end + kKT - 1) / kKT;
-  int pid_next = 0;
-  if (fast) {
-    load_tile_fast(0, page_of(tq0));
-    pid_next = page_of(kKT + tq0);
-  } else {
-    load_tile(0);
+    for (int j = 0; j < KS; ++j) koff[j] = i * PITCH + 16 * ((4 * j + G) ^ swz<D>(i));
+    const int k = i >> 2, q = i & 3, vr = 4 * G + k;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) voff[d] = vr * PITCH + 16 * ((2 * d + (q >> 1)) ^ swz<D>(vr)) + 8 * (q & 1);
   }
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();                 // the previous tile's LDS reads are done
-    stage_tile();
-    __syncthreads();
-    if (kt + 1 < ntiles) {           // in flight while this tile is computed
-      if (fast) {
-        load_tile_fast((kt + 1) * kKT, pid_next);
-        pid_next = page_of((kt + 2) * kKT + tq0);
-      } else {
-        load_tile((kt + 1) * kKT);
-      }
-    }
-    const int t0 = kt * kKT;
+
+  auto compute = [&](const unsigned char *kb, const unsigned char *vb, int t0) {
     // every position of the tile is seen by every row of the workgroup: no mask
     const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= pos_base + wg_row0);
 
@@ -249,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
       for (int rb = 0; rb < RB; ++rb) s[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        const u32x4 ka = *reinterpret_cast<const u32x4 *>(sm_k + (16 * mb + (lane & 15)) * KPITCH + 2 * (32 * j + 8 * (lane >> 4)));
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 16 * mb * PITCH);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           s[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[rb][j], s[rb][mb], 0, 0, 0);
@@ -305,32 +277,58 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
     for (int rb = 0; rb < RB; ++rb) {
       const float nm = m[rb] == -INFINITY ? 0.f : -m[rb];   // masked scores give exp2(-inf) = 0
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int r = 0; r < 4; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[rb][2 * kb + half][r], p.scale_log2, nm));
-            const float p1 = fast_exp2(fmaf(s[rb][2 * kb + half][r + 1], p.scale_log2, nm));
+            const float p0 = fast_exp2(fmaf(s[rb][2 * kb2 + half][r], p.scale_log2, nm));
+            const float p1 = fast_exp2(fmaf(s[rb][2 * kb2 + half][r + 1], p.scale_log2, nm));
             l[rb] += p0 + p1;
-            pb[rb][kb][2 * half + r / 2] = cvt_pk_bf16(p0, p1);
+            pb[rb][kb2][2 * half + r / 2] = cvt_pk_bf16(p0, p1);
           }
     }
     // O^T += V^T P^T over the tile's two 32-token k-blocks; one V^T read feeds RB products
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
       for (int i = 0; i < DB; ++i) {
-        const int vr = 16 * i + (lane & 15);
-        const unsigned char *vrow = sm_vt + vr * VPITCH;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + vt_col(vr, 32 * kb + 4 * (lane >> 4)));
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + vt_col(vr, 32 * kb + 16 + 4 * (lane >> 4)));
+        const unsigned char *vp = vb + voff[i] + 32 * kb2 * PITCH;
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4 *)(vp)));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4 *)(vp + 16 * PITCH)));
         const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          o[rb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb[rb][kb]), o[rb][i], 0, 0, 0);
+          o[rb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb[rb][kb2]), o[rb][i], 0, 0, 0);
       }
     }
+  };
+
+  // two tiles per trip, one per buffer; the barrier at each tile start waits
+  // for this tile's direct loads (all lanes) and for every wave to be done
+  // with the buffer that the next loads overwrite
+  const int ntiles = (kv_end + kKT - 1) / kKT;
+  if (ntiles > 0) {
+    fetch_pids(0);
+    issue(0, sm_k0, sm_v0);
+    fetch_pids(kKT);
+  }
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      issue((kt + 1) * kKT, sm_k1, sm_v1);
+      fetch_pids((kt + 2) * kKT);
+    }
+    compute(sm_k0, sm_v0, kt * kKT);
+    if (kt + 1 >= ntiles) break;
+    __syncthreads();
+    if (kt + 2 < ntiles) {
+      issue((kt + 2) * kKT, sm_k0, sm_v0);
+      fetch_pids((kt + 3) * kKT);
+    }
+    compute(sm_k1, sm_v1, (kt + 1) * kKT);
   }
 
   // row sums over the 4 lane groups, then the output rows
@@ -345,8 +343,8 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
       u32x2 w;
-      w[0] = f32_to_bf16_rne(o[rb][i][0] * inv) | (f32_to_bf16_rne(o[rb][i][1] * inv) << 16);
-      w[1] = f32_to_bf16_rne(o[rb][i][2] * inv) | (f32_to_bf16_rne(o[rb][i][3] * inv) << 16);
+      w[0] = cvt_pk_bf16(o[rb][i][0] * inv, o[rb][i][1] * inv);
+      w[1] = cvt_pk_bf16(o[rb][i][2] * inv, o[rb][i][3] * inv);
       *reinterpret_cast<u32x2 *>(orow + 16 * i + 4 * (lane >> 4)) = w;
     }
     if (p.lse && lane < 16)
@@ -374,7 +372,7 @@ hipError_t launch_paged_prefill(const PrefillParams &p, hipStream_t stream) {
 #define PKV_CASE(DD, HH, RR) \
   if (p.D == DD && HB == HH) return launch<DD, HH, RR>(p, stream);
   PKV_CASE(64, 1, 1) PKV_CASE(64, 2, 2) PKV_CASE(64, 4, 2)
-  PKV_CASE(128, 1, 1) PKV_CASE(128, 2, 1) PKV_CASE(128, 4, 1)
+  PKV_CASE(128, 1, 1) PKV_CASE(128, 2, 2) PKV_CASE(128, 4, 2)
 #undef PKV_CASE
   return hipErrorInvalidValue;
 }
