@@ -169,22 +169,50 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
   // (lrow = lane / LPR); the lane's 16 bytes land at physical chunk lane % LPR,
   // so it fetches the logical chunk that swz maps there.
   const int lrow = lane / LPR, pc = lane % LPR;
-  int pid[NI];                       // page ids of this lane's rows in the next tile to load
-  auto fetch_pids = [&](int t0) {
-#pragma unroll
-    for (int n = 0; n < NI; ++n) {
-      const int t = t0 + 16 * wave + n * RPI + lrow;
-      pid[n] = t < kv_end ? pt[t >> log2P] : 0;
-    }
+  // A wave loads 16 consecutive positions per tile; with pages of 16 or more
+  // tokens they share one page, whose id is wave-uniform and prefetched a
+  // tile ahead with a scalar load (its own counter, so waiting for it never
+  // waits for the direct loads in flight).
+  const bool big_pages = log2P >= 4;
+  // (read-only here: the constant address space lets the uniform load be scalar)
+  const __attribute__((address_space(4))) int32_t *pt_s =
+      (const __attribute__((address_space(4))) int32_t *)(pt);
+  int pid_next = 0;
+  auto fetch_pid = [&](int t0) {
+    const int t = t0 + 16 * wave;
+    pid_next = (big_pages && t < kv_end) ? pt_s[t >> log2P] : 0;
   };
   const u32x4 *fill = kFillRows;
+  // byte offset of this lane's chunk within a pool row, per load
+  int colb[NI];
+#pragma unroll
+  for (int n = 0; n < NI; ++n) colb[n] = 2 * (g * D + 8 * (pc ^ swz<D>(n * RPI + lrow)));
+  const unsigned row_bytes = unsigned(row_stride) * 2u;
+  const unsigned char *kbytes = reinterpret_cast<const unsigned char *>(p.k_pool);
+  const unsigned char *vbytes = reinterpret_cast<const unsigned char *>(p.v_pool);
   auto issue = [&](int t0, unsigned char *kb, unsigned char *vb) {
+    const int pid = __builtin_amdgcn_readfirstlane(pid_next);
+    if (big_pages && t0 + kKT <= kv_end && unsigned(pid) < unsigned(p.num_pages)) {
+      // the wave's 16 positions are inside the sequence, in one pool page
+      const unsigned row0 = (unsigned(pid) << log2P) | unsigned((t0 + 16 * wave) & pmask);
+#pragma unroll
+      for (int n = 0; n < NI; ++n) {
+        const uint64_t a = uint64_t(row0 + unsigned(n * RPI + lrow)) * row_bytes + unsigned(colb[n]);
+        const int dst = (16 * wave + n * RPI) * PITCH;
+        __builtin_amdgcn_global_load_lds(const_cast<unsigned char *>(kbytes + a), (PKV_LDS void *)(kb + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(const_cast<unsigned char *>(vbytes + a), (PKV_LDS void *)(vb + dst), 16, 0, 0);
+      }
+      return;
+    }
+    // general case: every lane looks its page up; positions past the end
+    // read zeros, a page id outside the pool reads NaN
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
       const int t = t0 + 16 * wave + n * RPI + lrow;
       const int c = pc ^ swz<D>(n * RPI + lrow);
-      const bool in_pool = t < kv_end && unsigned(pid[n]) < unsigned(p.num_pages);
-      const size_t off = ((size_t(in_pool ? pid[n] : 0) << log2P) + (t & pmask)) * row_stride +
+      const int pg = t < kv_end ? pt[t >> log2P] : 0;
+      const bool in_pool = t < kv_end && unsigned(pg) < unsigned(p.num_pages);
+      const size_t off = ((size_t(in_pool ? pg : 0) << log2P) + (t & pmask)) * row_stride +
                          size_t(g) * D + 8 * c;
       const u32x4 *alt = fill + (t < kv_end ? 1 : 0);
       const u32x4 *ks = in_pool ? reinterpret_cast<const u32x4 *>(p.k_pool + off) : alt;
@@ -193,6 +221,13 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
       __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(ks), (PKV_LDS void *)(kb + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(vs), (PKV_LDS void *)(vb + dst), 16, 0, 0);
     }
+  };
+  // The direct loads write LDS outside the compiler's memory model: each lane
+  // waits for its own loads before the barrier that hands the tile to the
+  // other waves.
+  auto tile_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
   // LDS read offsets.  K (A operand of S^T): row lane & 15 of a 16-row block,
@@ -311,24 +346,20 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
   // with the buffer that the next loads overwrite
   const int ntiles = (kv_end + kKT - 1) / kKT;
   if (ntiles > 0) {
-    fetch_pids(0);
+    fetch_pid(0);
     issue(0, sm_k0, sm_v0);
-    fetch_pids(kKT);
+    fetch_pid(kKT);
   }
   for (int kt = 0; kt < ntiles; kt += 2) {
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      issue((kt + 1) * kKT, sm_k1, sm_v1);
-      fetch_pids((kt + 2) * kKT);
-    }
+    tile_barrier();
+    if (kt + 1 < ntiles) issue((kt + 1) * kKT, sm_k1, sm_v1);
     compute(sm_k0, sm_v0, kt * kKT);
     if (kt + 1 >= ntiles) break;
-    __syncthreads();
-    if (kt + 2 < ntiles) {
-      issue((kt + 2) * kKT, sm_k0, sm_v0);
-      fetch_pids((kt + 3) * kKT);
-    }
+    fetch_pid((kt + 2) * kKT);       // its latency hides in the barrier's wait
+    tile_barrier();
+    if (kt + 2 < ntiles) issue((kt + 2) * kKT, sm_k0, sm_v0);
     compute(sm_k1, sm_v1, (kt + 1) * kKT);
+    fetch_pid((kt + 3) * kKT);
   }
 
   // row sums over the 4 lane groups, then the output rows
