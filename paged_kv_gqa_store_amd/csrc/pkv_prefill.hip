@@ -4,24 +4,26 @@
 // (packed [total_q, q_heads, head_dim] queries cut into 64-row Q tiles with a
 // tile -> (request, tile index) map; the paged KV source only translates
 // logical positions; HB = min(G, waves) q heads of one kv-head group packed
-// per workgroup so a K/V tile is read once for all of them; the grid is
-// (num_q_tiles * HB) x (kv_heads * ceil(G / HB))) and section "Python
-// Wrappers" (is_causal; scale 1/sqrt(head_dim)).  A request's query rows are
-// its last q_len positions: with the causal mask, row j of a request with
-// kv_len tokens sees positions <= kv_len - q_len + j.
+// per workgroup so a K/V tile is read once for all of them) and section
+// "Python Wrappers" (is_causal; scale 1/sqrt(head_dim)).  A request's query
+// rows are its last q_len positions: with the causal mask, row j of a request
+// with kv_len tokens sees positions <= kv_len - q_len + j.
 //
-// gfx950 design, per wave: 16 or 32 query rows (one or two 16-row blocks) of
-// one q head.
-//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16 with A = a 16-token block of the
-//                  K tile (LDS, row-major) and B = Q^T (registers, loaded once):
-//                  the output puts one query row per lane (lane & 15) and 4
-//                  tokens per register group, so the online softmax of a row
-//                  reduces over 16 registers and the 4 lane groups.
+// gfx950 design.  Both products run on the matrix cores with the softmax in
+// between kept per query row in registers:
+//   S^T = K Q^T    A = a block of tokens of the K tile (LDS, row-major),
+//                  B = Q^T (registers, loaded once); the output holds one
+//                  query row per lane and a run of tokens per register group.
 //   O^T += V^T P^T the probabilities are already in the B-operand layout of
-//                  P^T (8 tokens of the lane's row); A = V^T comes straight
-//                  from the row-major V tile through the LDS transpose read
-//                  (ds_read_b64_tr_b16).  P is rounded to bf16 for the matrix
-//                  core; the accumulators and the softmax statistics stay fp32.
+//                  P^T; A = V^T comes straight from the row-major V tile
+//                  through the LDS transpose read (ds_read_b64_tr_b16).  P is
+//                  rounded to bf16 for the matrix core; the accumulators and
+//                  the softmax statistics stay fp32.
+// With two or more q heads per kv head a wave owns 32 query rows of one head
+// and both products use v_mfma_f32_32x32x16_bf16, which sustains about twice
+// the rate of the 16x16x32 form on this chip; with one q head per kv head a
+// workgroup's 64 rows are spread over its 4 waves, 16 each, on the 16x16x32
+// form.
 // K and V tiles of 64 tokens move from the pool into LDS with direct loads
 // (global_load_lds_dwordx4: 16 bytes per lane, no registers, no staging
 // code), double-buffered, so one barrier per tile separates the loads of tile
@@ -41,6 +43,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -48,6 +51,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kQTile = PKV_PREFILL_TILE_ROWS;   // query rows per host tile
 constexpr int kKT = 64;                         // tokens per K/V tile
 constexpr int kThreads = 256;                   // 4 waves
+constexpr float kLazy = 8.f;                    // lazy rescale threshold (log2 units)
+
+#define PKV_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -76,125 +82,101 @@ __device__ __forceinline__ int swz(int r) {
 __device__ __attribute__((aligned(16))) u32x4 kFillRows[2] = {
     {0u, 0u, 0u, 0u}, {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}};
 
-#define PKV_LDS __attribute__((address_space(3)))
+// The workgroup's slice of the work: a q chunk of RW rows of one request for
+// HB q heads of one kv head.
+struct Slice {
+  int b, g, hg;              // request, kv head, group of HB q heads
+  int q0, q_len, kv_len;     // first packed row, rows and positions of the request
+  int wg_row0, wg_rows;      // the chunk's rows within the request
+  int pos_base;              // position of the request's row 0
+  int kv_end;                // positions the workgroup needs: [0, kv_end)
+};
 
-template <int D, int HB, int RB>
-__global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p) {
-  constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension
-  constexpr int DB = D / 16;                 // 16-dim blocks of the output
-  constexpr int PITCH = 2 * D;               // bytes per K/V row in LDS
-  constexpr int LPR = D / 8;                 // lanes (16-byte chunks) per row
-  constexpr int RPI = 64 / LPR;              // rows per direct load (64 lanes)
-  constexpr int NI = kKT / (4 * RPI);        // direct loads per wave, tile and tensor
-  constexpr int R = 16 * RB;                 // query rows per wave (RB blocks of 16)
-  constexpr int WPH = 4 / HB;                // waves per q head
-  constexpr int RW = WPH * R;                // query rows per workgroup and head
+// 1-D grid, XCD-aware: consecutive workgroup ids go round-robin to the 8 XCDs,
+// so id i takes logical slot (i % 8) * (n / 8) + i / 8 and each XCD runs a
+// contiguous slice of the logical order (kv-head group major, then q chunks),
+// whose workgroups read the same K/V rows through one L2.  The q chunks run
+// last-first: with the causal mask they are the longest.  Returns false for a
+// workgroup with no rows (the whole workgroup leaves).
+template <int HB, int RW>
+__device__ __forceinline__ bool locate(const PrefillParams &p, Slice &w) {
   constexpr int CH = kQTile / RW;            // workgroups along one host tile
-  static_assert(CH * RW == kQTile, "row split");
-  static_assert(16 % RPI == 0 || RPI == 16, "a wave loads whole 16-row groups");
-  // two buffers per tensor, separate objects so that reads of one buffer
-  // need not wait for the direct loads in flight into the other
-  __shared__ __attribute__((aligned(16))) unsigned char sm_k0[kKT * PITCH];
-  __shared__ __attribute__((aligned(16))) unsigned char sm_v0[kKT * PITCH];
-  __shared__ __attribute__((aligned(16))) unsigned char sm_k1[kKT * PITCH];
-  __shared__ __attribute__((aligned(16))) unsigned char sm_v1[kKT * PITCH];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // 1-D grid, XCD-aware: consecutive workgroup ids go round-robin to the 8
-  // XCDs, so id i is given logical slot (i % 8) * (n / 8) + i / 8 and each XCD
-  // runs a contiguous slice of the logical order (kv-head group major, then
-  // q chunks), whose workgroups read the same K/V rows through one L2.  The
-  // q chunks run last-first: with the causal mask they are the longest.
   const int hgroups = (p.G + HB - 1) / HB;
-  const int n_x = p.num_q_tiles * CH;                         // workgroups per group
+  const int n_x = p.num_q_tiles * CH;        // workgroups per group
   const unsigned nwg = gridDim.x, per_xcd = nwg / 8;
   const unsigned lin = blockIdx.x;
   const int logical = int(lin < 8 * per_xcd ? (lin % 8) * per_xcd + lin / 8 : lin);
   const int gy = logical / n_x, qx = n_x - 1 - logical % n_x;
   const int host_tile = qx / CH, chunk = qx % CH;
-  const int g = gy / hgroups, hg = gy % hgroups;
-  const int b = p.tile_to_batch[host_tile];
-  if (unsigned(b) >= unsigned(p.B)) return;                   // whole workgroup
+  w.g = gy / hgroups;
+  w.hg = gy % hgroups;
+  w.b = p.tile_to_batch[host_tile];
+  if (unsigned(w.b) >= unsigned(p.B)) return false;
   // rows past total_q and positions past the page table are never touched
-  const int q0 = min(max(p.qo_indptr[b], 0), p.total_q);
-  const int q_len = min(p.qo_indptr[b + 1], p.total_q) - q0;
-  const int kv_len = min(max(p.kv_lens[b], 0), p.max_pages << p.page_log2);
-  // rows of this workgroup within the request, and of this wave
-  const int wg_row0 = p.tile_to_index[host_tile] * kQTile + chunk * RW;
-  const int wg_rows = min(RW, q_len - wg_row0);
-  if (wg_row0 < 0 || wg_rows <= 0) return;                   // whole workgroup
-  const int h_in_group = hg * HB + wave / WPH;
-  const bool head_ok = h_in_group < p.G;
-  const int h = g * p.G + (head_ok ? h_in_group : 0);
-  const int row0 = wg_row0 + (wave % WPH) * R;               // first row of this wave
-  const int pos_base = kv_len - q_len;                        // position of row 0
-  int my_row[RB], my_pos[RB];
-  bool row_ok[RB];
+  w.q0 = min(max(p.qo_indptr[w.b], 0), p.total_q);
+  w.q_len = min(p.qo_indptr[w.b + 1], p.total_q) - w.q0;
+  w.kv_len = min(max(p.kv_lens[w.b], 0), p.max_pages << p.page_log2);
+  w.wg_row0 = p.tile_to_index[host_tile] * kQTile + chunk * RW;
+  w.wg_rows = min(RW, w.q_len - w.wg_row0);
+  if (w.wg_row0 < 0 || w.wg_rows <= 0) return false;
+  w.pos_base = w.kv_len - w.q_len;
+  w.kv_end = p.causal ? min(w.kv_len, w.pos_base + w.wg_row0 + w.wg_rows) : w.kv_len;
+  return true;
+}
+
+// Direct loads of one 64-token K/V tile into a pair of LDS buffers: load n of
+// a wave fills tile rows 16 * wave + n * RPI + lrow (lrow = lane / LPR); the
+// lane's 16 bytes land at physical chunk lane % LPR, so it fetches the
+// logical chunk that swz maps there.
+template <int D>
+struct TileLoader {
+  static constexpr int PITCH = 2 * D;        // bytes per K/V row in LDS
+  static constexpr int LPR = D / 8;          // lanes (16-byte chunks) per row
+  static constexpr int RPI = 64 / LPR;       // rows per direct load (64 lanes)
+  static constexpr int NI = kKT / (4 * RPI); // direct loads per wave, tile and tensor
+
+  const PrefillParams &p;
+  const int32_t *pt;                         // the request's page-table row
+  const __attribute__((address_space(4))) int32_t *pt_s;
+  int wave, lrow, pc, g, kv_end, log2P, pmask;
+  bool big_pages;
+  size_t row_stride;                         // elements per pool row (slot)
+  unsigned row_bytes;
+  int colb[NI];                              // byte offset of the lane's chunk in a pool row
+  int pid_next = 0;                          // page id of the wave's rows in the next tile
+
+  __device__ TileLoader(const PrefillParams &p_, const Slice &w, int wave_, int lane)
+      : p(p_), wave(wave_), g(w.g), kv_end(w.kv_end) {
+    log2P = p.page_log2;
+    pmask = (1 << log2P) - 1;
+    // A wave loads 16 consecutive positions per tile; with pages of 16 or
+    // more tokens they share one page, whose id is wave-uniform and read a
+    // tile ahead with a scalar load (its own counter, so waiting for it never
+    // waits for the direct loads in flight; the page table is read-only here,
+    // and the constant address space lets the uniform load be scalar).
+    big_pages = log2P >= 4;
+    pt = p.page_table + size_t(w.b) * p.max_pages;
+    pt_s = (const __attribute__((address_space(4))) int32_t *)(pt);
+    lrow = lane / LPR;
+    pc = lane % LPR;
+    row_stride = size_t(p.Hkv) * D;
+    row_bytes = unsigned(row_stride) * 2u;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    my_row[rb] = row0 + 16 * rb + (lane & 15);                // this lane's query rows
-    row_ok[rb] = head_ok && my_row[rb] < q_len;
-    my_pos[rb] = pos_base + my_row[rb];
+    for (int n = 0; n < NI; ++n) colb[n] = 2 * (g * D + 8 * (pc ^ swz<D>(n * RPI + lrow)));
   }
-  // positions the workgroup needs: [0, kv_end)
-  const int kv_end = p.causal ? min(kv_len, pos_base + wg_row0 + wg_rows) : kv_len;
-  const int log2P = p.page_log2, pmask = (1 << log2P) - 1;
-  const int32_t *pt = p.page_table + size_t(b) * p.max_pages;
-  const size_t row_stride = size_t(p.Hkv) * D;
 
-  // Q^T as the B operand: lane = query row (lane & 15), dims 32j + 8(lane >> 4)
-  bf16x8 qb[RB][KS];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row_ok[rb])
-        w = *reinterpret_cast<const u32x4 *>(p.q + (size_t(q0 + my_row[rb]) * p.Hq + h) * D + 32 * j + 8 * (lane >> 4));
-      qb[rb][j] = as_bf16x8(w);
-    }
-
-  float m[RB], l[RB];   // running max (log2 domain) and this lane's partial sum, per row block
-  f32x4 o[RB][DB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
-    l[rb] = 0.f;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[rb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // Direct loads: load n of this wave fills tile rows 16 * wave + n * RPI + lrow
-  // (lrow = lane / LPR); the lane's 16 bytes land at physical chunk lane % LPR,
-  // so it fetches the logical chunk that swz maps there.
-  const int lrow = lane / LPR, pc = lane % LPR;
-  // A wave loads 16 consecutive positions per tile; with pages of 16 or more
-  // tokens they share one page, whose id is wave-uniform and prefetched a
-  // tile ahead with a scalar load (its own counter, so waiting for it never
-  // waits for the direct loads in flight).
-  const bool big_pages = log2P >= 4;
-  // (read-only here: the constant address space lets the uniform load be scalar)
-  const __attribute__((address_space(4))) int32_t *pt_s =
-      (const __attribute__((address_space(4))) int32_t *)(pt);
-  int pid_next = 0;
-  auto fetch_pid = [&](int t0) {
+  __device__ __forceinline__ void fetch_pid(int t0) {
     const int t = t0 + 16 * wave;
     pid_next = (big_pages && t < kv_end) ? pt_s[t >> log2P] : 0;
-  };
-  const u32x4 *fill = kFillRows;
-  // byte offset of this lane's chunk within a pool row, per load
-  int colb[NI];
-#pragma unroll
-  for (int n = 0; n < NI; ++n) colb[n] = 2 * (g * D + 8 * (pc ^ swz<D>(n * RPI + lrow)));
-  const unsigned row_bytes = unsigned(row_stride) * 2u;
-  const unsigned char *kbytes = reinterpret_cast<const unsigned char *>(p.k_pool);
-  const unsigned char *vbytes = reinterpret_cast<const unsigned char *>(p.v_pool);
-  auto issue = [&](int t0, unsigned char *kb, unsigned char *vb) {
+  }
+
+  __device__ __forceinline__ void issue(int t0, unsigned char *kb, unsigned char *vb) {
     const int pid = __builtin_amdgcn_readfirstlane(pid_next);
     if (big_pages && t0 + kKT <= kv_end && unsigned(pid) < unsigned(p.num_pages)) {
       // the wave's 16 positions are inside the sequence, in one pool page
       const unsigned row0 = (unsigned(pid) << log2P) | unsigned((t0 + 16 * wave) & pmask);
+      const unsigned char *kbytes = reinterpret_cast<const unsigned char *>(p.k_pool);
+      const unsigned char *vbytes = reinterpret_cast<const unsigned char *>(p.v_pool);
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
         const uint64_t a = uint64_t(row0 + unsigned(n * RPI + lrow)) * row_bytes + unsigned(colb[n]);
@@ -214,21 +196,87 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
       const bool in_pool = t < kv_end && unsigned(pg) < unsigned(p.num_pages);
       const size_t off = ((size_t(in_pool ? pg : 0) << log2P) + (t & pmask)) * row_stride +
                          size_t(g) * D + 8 * c;
-      const u32x4 *alt = fill + (t < kv_end ? 1 : 0);
+      const u32x4 *alt = kFillRows + (t < kv_end ? 1 : 0);
       const u32x4 *ks = in_pool ? reinterpret_cast<const u32x4 *>(p.k_pool + off) : alt;
       const u32x4 *vs = in_pool ? reinterpret_cast<const u32x4 *>(p.v_pool + off) : alt;
       const int dst = (16 * wave + n * RPI) * PITCH;
       __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(ks), (PKV_LDS void *)(kb + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(vs), (PKV_LDS void *)(vb + dst), 16, 0, 0);
     }
-  };
-  // The direct loads write LDS outside the compiler's memory model: each lane
-  // waits for its own loads before the barrier that hands the tile to the
-  // other waves.
-  auto tile_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
+  }
+};
+
+// The direct loads write LDS outside the compiler's memory model: each lane
+// waits for its own loads before the barrier that hands the tile to the other
+// waves.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Two tiles per trip, one per LDS buffer pair; the barrier at each tile start
+// waits for this tile's direct loads (all lanes) and for every wave to be done
+// with the buffer pair that the next loads overwrite.  The page id of the tile
+// after next is fetched at the end of a tile, so its latency hides in the
+// barrier's wait.
+template <int D, class Compute>
+__device__ __forceinline__ void tile_loop(TileLoader<D> &ld, int kv_end, unsigned char *k0,
+                                          unsigned char *v0, unsigned char *k1, unsigned char *v1,
+                                          Compute &&compute) {
+  const int ntiles = (kv_end + kKT - 1) / kKT;
+  if (ntiles > 0) {
+    ld.fetch_pid(0);
+    ld.issue(0, k0, v0);
+    ld.fetch_pid(kKT);
+  }
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile_barrier();
+    if (kt + 1 < ntiles) ld.issue((kt + 1) * kKT, k1, v1);
+    compute(k0, v0, kt * kKT);
+    if (kt + 1 >= ntiles) break;
+    ld.fetch_pid((kt + 2) * kKT);
+    tile_barrier();
+    if (kt + 2 < ntiles) ld.issue((kt + 2) * kKT, k0, v0);
+    compute(k1, v1, (kt + 1) * kKT);
+    ld.fetch_pid((kt + 3) * kKT);
+  }
+}
+
+// One q head per kv head: 4 waves x 16 rows of a 64-row q chunk, each on the
+// 16x16x32 form (lane & 15 = query row, 4 tokens per register group).
+template <int D>
+__global__ __launch_bounds__(kThreads) void paged_prefill16_kernel(PrefillParams p) {
+  constexpr int KS = D / 32;                 // MFMA k-steps over the head dimension
+  constexpr int DB = D / 16;                 // 16-dim blocks of the output
+  constexpr int PITCH = TileLoader<D>::PITCH;
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k0[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v0[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k1[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v1[kKT * PITCH];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Slice w;
+  if (!locate<1, kQTile>(p, w)) return;
+  const int h = w.g * p.G + w.hg;            // G == 1: the kv head's only q head
+  const int my_row = w.wg_row0 + 16 * wave + (lane & 15);
+  const bool row_ok = my_row < w.q_len;
+  const int my_pos = w.pos_base + my_row;
+  const int kv_end = w.kv_end;
+
+  // Q^T as the B operand: lane = query row (lane & 15), dims 32j + 8(lane >> 4)
+  bf16x8 qb[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row_ok)
+      v = *reinterpret_cast<const u32x4 *>(p.q + (size_t(w.q0 + my_row) * p.Hq + h) * D + 32 * j + 8 * (lane >> 4));
+    qb[j] = as_bf16x8(v);
+  }
+  float m = -INFINITY, l = 0.f;              // running max (log2 domain), lane's partial sum
+  f32x4 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // LDS read offsets.  K (A operand of S^T): row lane & 15 of a 16-row block,
   // logical chunk 4j + (lane >> 4).  V (transpose read): lane 4k + q of
@@ -245,165 +293,273 @@ __global__ __launch_bounds__(kThreads) void paged_prefill_kernel(PrefillParams p
 
   auto compute = [&](const unsigned char *kb, const unsigned char *vb, int t0) {
     // every position of the tile is seen by every row of the workgroup: no mask
-    const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= pos_base + wg_row0);
-
-    // S^T for 4 blocks of 16 tokens: lane holds tokens 16mb + 4(lane >> 4) + r of
-    // row (lane & 15) of each row block; one K read from LDS feeds RB products
-    f32x4 s[RB][4];
+    const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= w.pos_base + w.wg_row0);
+    // S^T for 4 blocks of 16 tokens: lane holds tokens 16mb + 4(lane >> 4) + r
+    f32x4 s[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         const u32x4 ka = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 16 * mb * PITCH);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          s[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[rb][j], s[rb][mb], 0, 0, 0);
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
       }
+    }
+    // mask, then the tile max of this lane's row on the raw scores (scale > 0)
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!full_tile) {
+          const int pos = t0 + 16 * mb + 4 * (lane >> 4) + r;
+          const bool seen = pos < kv_end && (!p.causal || pos <= my_pos);
+          s[mb][r] = seen ? s[mb][r] : -INFINITY;
+        }
+        tmax = fmaxf(tmax, s[mb][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // The running max moves only when a row's tile max passes it by more than
+    // kLazy: until then the probabilities are taken against the old max (at
+    // most 2^kLazy) and the accumulators need no rescale; o / l is the same
+    // quotient either way.
+    const float ts = tmax * p.scale_log2;
+    if (__any(ts > m + kLazy)) {             // wave-uniform
+      const float mn = fmaxf(m, ts);
+      const float alpha = (m == mn) ? 1.f : fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) o[i] *= alpha;
     }
     // probabilities in the B layout of P^T: k-slot 8(lane >> 4) + i <-> token
-    // 32kb + 4(lane >> 4) + i (i < 4) or 32kb + 16 + 4(lane >> 4) + i - 4.
-    // The running max m (log2 domain) moves only when a row's tile max passes
-    // it by more than kLazy: until then the probabilities are taken against
-    // the old max (at most 2^kLazy, exact in fp32 and bf16 range) and the
-    // accumulators need no rescale; o / l is the same quotient either way.
-    constexpr float kLazy = 8.f;
-    float ts[RB];
-    bool grow = false;
+    // 32kb + 4(lane >> 4) + i (i < 4) or 32kb + 16 + 4(lane >> 4) + i - 4
+    const float nm = m == -INFINITY ? 0.f : -m;   // masked scores give exp2(-inf) = 0
+    u32x4 pb[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // mask, then the tile max of this lane's row on the raw scores (scale > 0)
-      float tmax = -INFINITY;
-      if (full_tile) {
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[rb][mb][r]);
-      } else {
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = fast_exp2(fmaf(s[2 * kb2 + half][r], p.scale_log2, nm));
+          const float p1 = fast_exp2(fmaf(s[2 * kb2 + half][r + 1], p.scale_log2, nm));
+          l += p0 + p1;
+          pb[kb2][2 * half + r / 2] = cvt_pk_bf16(p0, p1);
+        }
+    // O^T += V^T P^T over the tile's two 32-token k-blocks
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int pos = t0 + 16 * mb + 4 * (lane >> 4) + r;
-            const bool seen = pos < kv_end && (!p.causal || pos <= my_pos[rb]);
-            s[rb][mb][r] = seen ? s[rb][mb][r] : -INFINITY;
-            tmax = fmaxf(tmax, s[rb][mb][r]);
-          }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      ts[rb] = tmax * p.scale_log2;
-      grow |= ts[rb] > m[rb] + kLazy;
-    }
-    if (__any(grow)) {               // wave-uniform: rescale every row block
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float mn = fmaxf(m[rb], ts[rb]);
-        const float alpha = (m[rb] == mn) ? 1.f : fast_exp2(m[rb] - mn);
-        m[rb] = mn;
-        l[rb] *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) o[rb][i] *= alpha;
-      }
-    }
-    u32x4 pb[RB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float nm = m[rb] == -INFINITY ? 0.f : -m[rb];   // masked scores give exp2(-inf) = 0
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[rb][2 * kb2 + half][r], p.scale_log2, nm));
-            const float p1 = fast_exp2(fmaf(s[rb][2 * kb2 + half][r + 1], p.scale_log2, nm));
-            l[rb] += p0 + p1;
-            pb[rb][kb2][2 * half + r / 2] = cvt_pk_bf16(p0, p1);
-          }
-    }
-    // O^T += V^T P^T over the tile's two 32-token k-blocks; one V^T read feeds RB products
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int i = 0; i < DB; ++i) {
         const unsigned char *vp = vb + voff[i] + 32 * kb2 * PITCH;
-        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (PKV_LDS i16x4 *)(vp)));
-        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (PKV_LDS i16x4 *)(vp + 16 * PITCH)));
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4 *)(vp)));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4 *)(vp + 16 * PITCH)));
         const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          o[rb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb[rb][kb2]), o[rb][i], 0, 0, 0);
+        o[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb[kb2]), o[i], 0, 0, 0);
       }
-    }
   };
+  TileLoader<D> ld(p, w, wave, lane);
+  tile_loop<D>(ld, kv_end, sm_k0, sm_v0, sm_k1, sm_v1, compute);
 
-  // two tiles per trip, one per buffer; the barrier at each tile start waits
-  // for this tile's direct loads (all lanes) and for every wave to be done
-  // with the buffer that the next loads overwrite
-  const int ntiles = (kv_end + kKT - 1) / kKT;
-  if (ntiles > 0) {
-    fetch_pid(0);
-    issue(0, sm_k0, sm_v0);
-    fetch_pid(kKT);
-  }
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    tile_barrier();
-    if (kt + 1 < ntiles) issue((kt + 1) * kKT, sm_k1, sm_v1);
-    compute(sm_k0, sm_v0, kt * kKT);
-    if (kt + 1 >= ntiles) break;
-    fetch_pid((kt + 2) * kKT);       // its latency hides in the barrier's wait
-    tile_barrier();
-    if (kt + 2 < ntiles) issue((kt + 2) * kKT, sm_k0, sm_v0);
-    compute(sm_k1, sm_v1, (kt + 1) * kKT);
-    fetch_pid((kt + 3) * kKT);
-  }
-
-  // row sums over the 4 lane groups, then the output rows
+  // row sums over the 4 lane groups, then the output row
+  float lsum = l;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (!row_ok) return;
+  const float inv = 1.f / lsum;
+  uint16_t *orow = p.out + (size_t(w.q0 + my_row) * p.Hq + h) * D;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float lsum = l[rb];
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (!row_ok[rb]) continue;
-    const float inv = 1.f / lsum;
-    uint16_t *orow = p.out + (size_t(q0 + my_row[rb]) * p.Hq + h) * D;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) {
-      u32x2 w;
-      w[0] = cvt_pk_bf16(o[rb][i][0] * inv, o[rb][i][1] * inv);
-      w[1] = cvt_pk_bf16(o[rb][i][2] * inv, o[rb][i][3] * inv);
-      *reinterpret_cast<u32x2 *>(orow + 16 * i + 4 * (lane >> 4)) = w;
-    }
-    if (p.lse && lane < 16)
-      p.lse[size_t(q0 + my_row[rb]) * p.Hq + h] = (m[rb] + __builtin_amdgcn_logf(lsum)) * kLn2;
+  for (int i = 0; i < DB; ++i) {
+    u32x2 v;
+    v[0] = cvt_pk_bf16(o[i][0] * inv, o[i][1] * inv);
+    v[1] = cvt_pk_bf16(o[i][2] * inv, o[i][3] * inv);
+    *reinterpret_cast<u32x2 *>(orow + 16 * i + 4 * (lane >> 4)) = v;
   }
+  if (p.lse && lane < 16)
+    p.lse[size_t(w.q0 + my_row) * p.Hq + h] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
-template <int D, int HB, int RB>
-hipError_t launch(const PrefillParams &p, hipStream_t stream) {
-  constexpr int CH = kQTile / ((4 / HB) * 16 * RB);
+// Two or more q heads per kv head: a wave owns 32 query rows of one head, on
+// the 32x32x16 form (lane & 31 = query row; register r of a 32-token block is
+// token 8(r / 4) + 4(lane >> 5) + r % 4).  HB heads per workgroup, 4 / HB
+// waves per head.
+template <int D, int HB>
+__global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams p) {
+  constexpr int KS = D / 16;                 // k-steps of S^T over the head dimension
+  constexpr int MB = D / 32;                 // 32-dim blocks of O^T
+  constexpr int WPH = 4 / HB;                // waves per q head
+  constexpr int RW = WPH * 32;               // query rows per workgroup and head
+  static_assert(kQTile % RW == 0, "row split");
+  constexpr int PITCH = TileLoader<D>::PITCH;
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k0[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v0[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k1[kKT * PITCH];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v1[kKT * PITCH];
+
+  const int lane = threadIdx.x & 63, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Slice w;
+  if (!locate<HB, RW>(p, w)) return;
+  const int h_in_group = w.hg * HB + wave / WPH;
+  const bool head_ok = h_in_group < p.G;
+  const int h = w.g * p.G + (head_ok ? h_in_group : 0);
+  const int my_row = w.wg_row0 + (wave % WPH) * 32 + (lane & 31);
+  const bool row_ok = head_ok && my_row < w.q_len;
+  const int my_pos = w.pos_base + my_row;
+  const int kv_end = w.kv_end;
+
+  // Q^T as the B operand: lane = query row (lane & 31), dims 16j + 8(lane >> 5)
+  bf16x8 qb[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row_ok)
+      v = *reinterpret_cast<const u32x4 *>(p.q + (size_t(w.q0 + my_row) * p.Hq + h) * D + 16 * j + 8 * hl);
+    qb[j] = as_bf16x8(v);
+  }
+  float m = -INFINITY, l = 0.f;              // running max (log2 domain), lane's partial sum
+  f32x16 o[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+
+  // LDS read offsets.  K (A operand of S^T): row lane & 31 of a 32-row block,
+  // logical chunk 2j + (lane >> 5).  V (transpose read, A operand of O^T):
+  // lane 4k + q of the 16-lane group (hl, u) points at tile row 4hl + k (lo)
+  // or 8 + 4hl + k (hi) of a 16-row block, dims 32i + 16u + 4q .. + 3.
+  int koff[KS], vlo[MB], vhi[MB];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) koff[j] = r * PITCH + 16 * ((2 * j + hl) ^ swz<D>(r & 15));
+    const int u = (lane >> 4) & 1, i = lane & 15, k = i >> 2, q = i & 3;
+    const int r_lo = 4 * hl + k, r_hi = 8 + 4 * hl + k;
+#pragma unroll
+    for (int d = 0; d < MB; ++d) {
+      const int c = 4 * d + 2 * u + (q >> 1);
+      vlo[d] = r_lo * PITCH + 16 * (c ^ swz<D>(r_lo)) + 8 * (q & 1);
+      vhi[d] = r_hi * PITCH + 16 * (c ^ swz<D>(r_hi)) + 8 * (q & 1);
+    }
+  }
+
+  auto compute = [&](const unsigned char *kb, const unsigned char *vb, int t0) {
+    const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= w.pos_base + w.wg_row0);
+    // S^T for 2 blocks of 32 tokens
+    f32x16 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 32 * mb * PITCH);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (!full_tile) {
+          const int pos = t0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool seen = pos < kv_end && (!p.causal || pos <= my_pos);
+          s[mb][r] = seen ? s[mb][r] : -INFINITY;
+        }
+        tmax = fmaxf(tmax, s[mb][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float ts = tmax * p.scale_log2;
+    if (__any(ts > m + kLazy)) {             // wave-uniform lazy rescale
+      const float mn = fmaxf(m, ts);
+      const float alpha = (m == mn) ? 1.f : fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) o[i] *= alpha;
+    }
+    // P^T as the B operand of 4 k-steps of 16 tokens: k-slot 8(lane >> 5) + e
+    // of step st <-> token 16st + 4(lane >> 5) + e (e < 4) or 16st + 8 +
+    // 4(lane >> 5) + e - 4, i.e. register groups 2(st % 2) and 2(st % 2) + 1
+    // of block st / 2
+    const float nm = m == -INFINITY ? 0.f : -m;
+    u32x4 pb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int r = 8 * (st & 1) + e;
+        const float p0 = fast_exp2(fmaf(s[st >> 1][r], p.scale_log2, nm));
+        const float p1 = fast_exp2(fmaf(s[st >> 1][r + 1], p.scale_log2, nm));
+        l += p0 + p1;
+        pb[st][e >> 1] = cvt_pk_bf16(p0, p1);
+      }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4 *)(vb + vlo[i] + 16 * st * PITCH)));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PKV_LDS i16x4 *)(vb + vhi[i] + 16 * st * PITCH)));
+        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[st]), o[i], 0, 0, 0);
+      }
+  };
+  TileLoader<D> ld(p, w, wave, lane);
+  tile_loop<D>(ld, kv_end, sm_k0, sm_v0, sm_k1, sm_v1, compute);
+
+  const float lsum = l + __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const float inv = 1.f / lsum;
+  uint16_t *orow = p.out + (size_t(w.q0 + my_row) * p.Hq + h) * D;
+  // register 4q + e of block i is dim 32i + 8q + 4(lane >> 5) + e
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x2 v;
+      v[0] = cvt_pk_bf16(o[i][4 * q] * inv, o[i][4 * q + 1] * inv);
+      v[1] = cvt_pk_bf16(o[i][4 * q + 2] * inv, o[i][4 * q + 3] * inv);
+      *reinterpret_cast<u32x2 *>(orow + 32 * i + 8 * q + 4 * hl) = v;
+    }
+  if (p.lse && lane < 32)
+    p.lse[size_t(w.q0 + my_row) * p.Hq + h] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
+}
+
+template <int D>
+hipError_t launch16(const PrefillParams &p, hipStream_t stream) {
+  const dim3 grid{unsigned(p.num_q_tiles * p.Hkv * p.G)}, block{kThreads};
+  hipLaunchKernelGGL((paged_prefill16_kernel<D>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int HB>
+hipError_t launch32(const PrefillParams &p, hipStream_t stream) {
+  constexpr int CH = kQTile / ((4 / HB) * 32);
   const int hgroups = (p.G + HB - 1) / HB;
   const dim3 grid{unsigned(p.num_q_tiles * CH * p.Hkv * hgroups)}, block{kThreads};
-  hipLaunchKernelGGL((paged_prefill_kernel<D, HB, RB>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((paged_prefill32_kernel<D, HB>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_paged_prefill(const PrefillParams &p, hipStream_t stream) {
-  // HB = min(G, 4) q heads per workgroup.  At D = 64 a wave takes two 16-row
-  // blocks once a workgroup holds two or more heads (one K/V^T read from LDS
-  // then feeds two products); at D = 128 the second block's registers would
-  // leave one wave per SIMD, which measured slower, so a wave keeps one block.
+  // HB = min(G, 4) q heads per workgroup share each K/V tile.
   const int HB = p.G < 4 ? p.G : 4;
-#define PKV_CASE(DD, HH, RR) \
-  if (p.D == DD && HB == HH) return launch<DD, HH, RR>(p, stream);
-  PKV_CASE(64, 1, 1) PKV_CASE(64, 2, 2) PKV_CASE(64, 4, 2)
-  PKV_CASE(128, 1, 1) PKV_CASE(128, 2, 2) PKV_CASE(128, 4, 2)
+  if (HB == 1) {
+    if (p.D == 64) return launch16<64>(p, stream);
+    if (p.D == 128) return launch16<128>(p, stream);
+    return hipErrorInvalidValue;
+  }
+#define PKV_CASE(DD, HH) \
+  if (p.D == DD && HB == HH) return launch32<DD, HH>(p, stream);
+  PKV_CASE(64, 2) PKV_CASE(64, 4) PKV_CASE(128, 2) PKV_CASE(128, 4)
 #undef PKV_CASE
   return hipErrorInvalidValue;
 }
