@@ -110,6 +110,33 @@ def time_launches(fn, reps: int, warmup: int = 3) -> float:
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+def time_graph_launches(fn, n: int) -> float:
+    """Mean µs per call of ``fn`` over ``n`` calls captured back to back in one
+    HIP graph, from HIP events around its replay on the current stream: the
+    kernel's duration without the per-launch dispatch gap of eager launches."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        for i in range(n):               # eager pass first: code objects load outside capture
+            fn(i)
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
 def measure_extras(args, pkv, W, dev, to_bf16, to_i32) -> dict:
     """Secondary rows of the path, each on its own synthetic workload."""
     import torch
@@ -234,6 +261,7 @@ def main():
     # server, and the figure `value` and `ms_per_step` report unless --eager.
     eager_ms_per_step = ms_per_step
     launch = "eager"
+    attn_graph_us = None
     if not args.eager:
         from paged_kv_gqa_store_amd.graph import StepGraph
         g = StepGraph([pools[i % len(pools)] for i in range(args.steps)], q, k_new, v_new,
@@ -253,6 +281,14 @@ def main():
             f"(wall; events {ge0.elapsed_time(ge1) * 1e3 / args.steps:.1f} us) vs {eager_ms_per_step * 1e3:.1f} us eager")
         launch = f"hip_graph ({args.steps} steps per replay)"
         del g
+        # the attention kernel alone, K launches back to back in one graph
+        # (rotating pools as above): its average duration for the roofline
+        attn_graph_us = time_graph_launches(lambda i: pkv.paged_decode_attn(
+            q, pools[i % len(pools)][0], pools[i % len(pools)][1], page_table, seq_lens, max_len, S,
+            o_partial=o_p, lse_partial=l_p), args.steps)
+        achieved = attn_kernel_b / (attn_graph_us * 1e-6) / 1e9
+        log(f"[bench] attention kernel alone, {args.steps} launches in one graph: {attn_graph_us:.1f} us per launch, "
+            f"{achieved:.0f} GB/s = {achieved / PEAK_HBM_GBPS:.1%} of {PEAK_HBM_GBPS:.0f} GB/s")
 
     # kv_store bandwidth: bulk fill of every position (prefill-style), same kernel and ABI
     k_rows, v_rows, bslots = W.bulk_fill_rows(inp)
@@ -330,6 +366,7 @@ def main():
                             "the K timed steps run as one HIP graph replay unless launch says eager",
         "attn_us_per_step": round(attn_us + float(merge_ms.mean() * 1e3), 2),
         "attn_kernel_us": round(attn_us, 2),
+        "attn_kernel_graph_us": None if attn_graph_us is None else round(attn_graph_us, 2),
         "merge_kernel_us": round(float(merge_ms.mean() * 1e3), 2),
         "store_step_us": round(float(store_ms.mean() * 1e3), 2),
         "attn_kv_GBps": round(kv_b / ((attn_us + merge_ms.mean() * 1e3) * 1e-6) / 1e9, 1),
@@ -345,6 +382,9 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": attn_kernel_b,
+            "duration_us": round(attn_us if attn_graph_us is None else attn_graph_us, 2),
+            "duration_from": ("HIP events around each eager launch" if attn_graph_us is None else
+                              f"HIP events around one graph of {args.steps} back-to-back launches"),
         },
     }
 
