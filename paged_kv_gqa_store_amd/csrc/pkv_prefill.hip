@@ -307,17 +307,20 @@ __global__ __launch_bounds__(kThreads) void paged_prefill16_kernel(PrefillParams
     }
     // mask, then the tile max of this lane's row on the raw scores (scale > 0)
     float tmax = -INFINITY;
+    if (!full_tile) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (!full_tile) {
+        for (int r = 0; r < 4; ++r) {
           const int pos = t0 + 16 * mb + 4 * (lane >> 4) + r;
           const bool seen = pos < kv_end && (!p.causal || pos <= my_pos);
           s[mb][r] = seen ? s[mb][r] : -INFINITY;
         }
-        tmax = fmaxf(tmax, s[mb][r]);
-      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[mb][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     // The running max moves only when a row's tile max passes it by more than
@@ -448,29 +451,34 @@ __global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams
   auto compute = [&](const unsigned char *kb, const unsigned char *vb, int t0) {
     const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= w.pos_base + w.wg_row0);
     // S^T for 2 blocks of 32 tokens
+    // (the two blocks are independent chains, interleaved k-step by k-step)
     f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
-#pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 32 * mb * PITCH);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
-      }
-    }
-    float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (!full_tile) {
+      for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 32 * mb * PITCH);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
+      }
+    float tmax = -INFINITY;
+    if (!full_tile) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int pos = t0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
           const bool seen = pos < kv_end && (!p.causal || pos <= my_pos);
           s[mb][r] = seen ? s[mb][r] : -INFINITY;
         }
-        tmax = fmaxf(tmax, s[mb][r]);
-      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float ts = tmax * p.scale_log2;
     if (__any(ts > m + kLazy)) {             // wave-uniform lazy rescale
@@ -499,9 +507,9 @@ __global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams
       }
     // O^T += V^T P^T
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      for (int i = 0; i < MB; ++i) {
         const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (PKV_LDS i16x4 *)(vb + vlo[i] + 16 * st * PITCH)));
         const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
