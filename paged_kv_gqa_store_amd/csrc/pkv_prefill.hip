@@ -64,6 +64,17 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// max / sum of x over lanes l and l ^ 32 on the VALU: v_permlane32_swap on two
+// copies of x leaves {x[l % 32], x[l % 32 + 32]} in the pair, on every lane
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // 16-byte chunk permutation of K/V row r (only r & 15 matters): an XOR with a
 // bit shuffle of r such that chunk c of 16 consecutive rows lands on distinct
 // chunks, and so do chunks {2i, 2i + 1} of rows 4a .. 4a + 3 (D = 128: 16
@@ -457,13 +468,20 @@ __global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+    // (the next k-step's K fragments are read while this one's products run)
+    u32x4 ka[2][2];
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
+    for (int mb = 0; mb < 2; ++mb) ka[0][mb] = *reinterpret_cast<const u32x4 *>(kb + koff[0] + 32 * mb * PITCH);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 32 * mb * PITCH);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
-      }
+    for (int j = 0; j < KS; ++j) {
+      if (j + 1 < KS)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          ka[(j + 1) & 1][mb] = *reinterpret_cast<const u32x4 *>(kb + koff[j + 1] + 32 * mb * PITCH);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[j & 1][mb]), qb[j], s[mb], 0, 0, 0);
+    }
     float tmax = -INFINITY;
     if (!full_tile) {
 #pragma unroll
@@ -479,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_xor32(tmax);
     const float ts = tmax * p.scale_log2;
     if (__any(ts > m + kLazy)) {             // wave-uniform lazy rescale
       const float mn = fmaxf(m, ts);
@@ -521,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams
   TileLoader<D> ld(p, w, wave, lane);
   tile_loop<D>(ld, kv_end, sm_k0, sm_v0, sm_k1, sm_v1, compute);
 
-  const float lsum = l + __shfl_xor(l, 32);
+  const float lsum = sum_xor32(l);
   if (!row_ok) return;
   const float inv = 1.f / lsum;
   uint16_t *orow = p.out + (size_t(w.q0 + my_row) * p.Hq + h) * D;
