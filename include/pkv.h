@@ -10,6 +10,7 @@
  *   pkv_indexing          row gather from a vocabulary slice (embedding lookup)
  *   pkv_paged_decode_attn split-KV attention through the page table -> partials
  *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
+ *   pkv_paged_decode_attn_merged  the attention and the merge in one call
  *   pkv_num_splits        split-count heuristic (host only)
  *   pkv_split_chunk       positions per split for a split count (host only)
  *   pkv_status_str        text of a status code
@@ -249,6 +250,31 @@ pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *
 pkv_status pkv_decode_merge(const float *o_partial, const float *lse_partial, int32_t B,
                             int32_t Hq, int32_t D, int32_t num_splits, void *out, float *lse_out,
                             void *stream);
+
+/*
+ * pkv_paged_decode_attn_merged -- pkv_paged_decode_attn followed by
+ * pkv_decode_merge, in one call, with the same results bit for bit.
+ *
+ * Follows the same passages as those two calls (AstrAI "CUDA Kernels",
+ * "Q Scheduling and KV Addressing"; cuDNN frontend "CSA Fused Compressor",
+ * "ratio=128" and "Numerics").  With num_splits == 1 the merge of a single
+ * split is its own output (weight exp(0) = 1): one kernel writes out (and
+ * lse_out) directly, without partials, and o_partial / lse_partial may be
+ * NULL.  With num_splits > 1 the attention writes the partials (required)
+ * and the merge runs as a second launch on the same stream.
+ *   Arguments as pkv_paged_decode_attn, plus
+ *   out      device bf16 [B, Hq, D], 16-byte aligned
+ *   lse_out  device fp32 [B, Hq] or NULL
+ * Status codes as the two calls; nothing is launched on an error.
+ */
+pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const void *v_pool,
+                                        const int32_t *page_table, const int32_t *seq_lens,
+                                        int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t page_size, int32_t num_pages,
+                                        int32_t max_pages_per_seq, int32_t max_seq_len,
+                                        int32_t num_splits, float scale, float *o_partial,
+                                        float *lse_partial, void *out, float *lse_out,
+                                        void *stream);
 
 /*
  * pkv_num_splits -- split count for a batch (host only, no GPU call).

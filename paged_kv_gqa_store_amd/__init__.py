@@ -7,6 +7,9 @@ One decode step is three hand-written HIP kernels behind a C ABI
 * ``paged_decode_attn``  split-KV attention over pages found through a page table;
 * ``decode_merge``       log-sum-exp merge of the split partials;
 
+(``paged_decode_attn_merged`` runs the last two as one call: a single kernel
+when there is one split),
+
 plus ``paged_prefill_attn`` (packed multi-token queries over the same pool,
 with the ``prefill_plan`` work map), ``kv_store_rope`` (the store with K rotated by a rotary embedding on the
 way, and ``paged_decode_attn(..., q_positions=...)`` rotating q in the
@@ -21,5 +24,6 @@ fallback implementation.
 """
 from .ops import (  # noqa: F401
     PrefillPlan, decode_merge, decode_step, indexing, kv_store, kv_store_rope, num_splits,
-    paged_decode_attn, paged_prefill_attn, prefill_plan, split_chunk, workspace,
+    paged_decode_attn, paged_decode_attn_merged, paged_prefill_attn, prefill_plan, split_chunk,
+    workspace,
 )

@@ -41,7 +41,8 @@ pkv_status attention_params(const void *q, const void *k_pool, const void *v_poo
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
                             int32_t num_pages, int32_t max_pages_per_seq, int32_t max_seq_len,
                             int32_t num_splits, float scale, float *o_partial,
-                            float *lse_partial, pkv::DecodeParams &p) {
+                            float *lse_partial, pkv::DecodeParams &p,
+                            bool need_partials = true) {
   if (B < 0 || Hq < 1 || Hkv < 1 || num_pages < 1 || max_pages_per_seq < 1 || max_seq_len < 0 ||
       num_splits < 1 || num_splits > kMaxSplits)
     return PKV_ERR_SHAPE;
@@ -59,8 +60,8 @@ pkv_status attention_params(const void *q, const void *k_pool, const void *v_poo
   p = pkv::DecodeParams{};
   p.B = B;
   if (B == 0) return PKV_OK;
-  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !o_partial || !lse_partial)
-    return PKV_ERR_NULL;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens) return PKV_ERR_NULL;
+  if (need_partials && (!o_partial || !lse_partial)) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_ALIGN;
   p.q = static_cast<const uint16_t *>(q);
   p.k_pool = static_cast<const uint16_t *>(k_pool);
@@ -319,6 +320,36 @@ pkv_status pkv_paged_prefill_attn(const void *q, const void *k_pool, const void 
   p.causal = causal ? 1 : 0;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = pkv::launch_paged_prefill(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const void *v_pool,
+                                        const int32_t *page_table, const int32_t *seq_lens,
+                                        int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t page_size, int32_t num_pages,
+                                        int32_t max_pages_per_seq, int32_t max_seq_len,
+                                        int32_t num_splits, float scale, float *o_partial,
+                                        float *lse_partial, void *out, float *lse_out,
+                                        void *stream) {
+  pkv::DecodeParams p;
+  const bool one = num_splits == 1;
+  pkv_status st = attention_params(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D,
+                                   page_size, num_pages, max_pages_per_seq, max_seq_len,
+                                   num_splits, scale, o_partial, lse_partial, p, !one);
+  if (st != PKV_OK || p.B == 0) return st;
+  if (!out) return PKV_ERR_NULL;
+  if (!aligned16(out)) return PKV_ERR_ALIGN;
+  if (int64_t(B) * Hq > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
+  if (!one && !aligned16(o_partial)) return PKV_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (one) {
+    p.out = static_cast<uint16_t *>(out);
+    p.lse_out = lse_out;
+    return pkv::launch_paged_decode_mfma(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  }
+  if (pkv::launch_paged_decode(p, s) != hipSuccess) return PKV_ERR_HIP;
+  const hipError_t e = pkv::launch_decode_merge(o_partial, lse_partial, B * Hq, D, num_splits,
+                                                static_cast<uint16_t *>(out), lse_out, s);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -369,13 +369,19 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
       M = fmaxf(M, sm_m[w][h]);
       nan |= sm_l[w][h] != sm_l[w][h];
     }
-    const size_t orow = (size_t(b) * p.Hq + size_t(g) * G + h) * p.num_splits + s;
+    const size_t frow = size_t(b) * p.Hq + size_t(g) * G + h;   // (b, q head)
+    const size_t orow = frow * p.num_splits + s;
     // Empty split: no position seen.  A split whose every score was NaN also
     // leaves the running max at -inf (fmaxf drops NaN) but its sum is NaN, and
     // it must come out NaN, so it takes the general path (NaN * 0 stays NaN).
     if (M == -INFINITY && !nan) {
-      p.o_partial[orow * D + d] = 0.f;
-      if (d == 0) p.lse_partial[orow] = -INFINITY;
+      if (p.out) {
+        p.out[frow * D + d] = 0;
+        if (d == 0 && p.lse_out) p.lse_out[frow] = -INFINITY;
+      } else {
+        p.o_partial[orow * D + d] = 0.f;
+        if (d == 0) p.lse_partial[orow] = -INFINITY;
+      }
       continue;
     }
     float l = 0.f, o = 0.f;
@@ -386,8 +392,17 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
       l = fmaf(sm_l[w][h], f, l);
       o = fmaf(sm_acc[w][h][d], f, o);
     }
-    p.o_partial[orow * D + d] = o / l;
-    if (d == 0) p.lse_partial[orow] = (M + __builtin_amdgcn_logf(l)) * kLn2;
+    const float lse = (M + __builtin_amdgcn_logf(l)) * kLn2;
+    if (p.out) {
+      // the merge of one split: weight exp(lse - lse) = 1, so out is this
+      // split's output rounded once, and a NaN lse gives the canonical NaN
+      const bool bad = lse != lse;
+      p.out[frow * D + d] = uint16_t(f32_to_bf16_rne(bad ? NAN : o / l));
+      if (d == 0 && p.lse_out) p.lse_out[frow] = bad ? NAN : lse;
+    } else {
+      p.o_partial[orow * D + d] = o / l;
+      if (d == 0) p.lse_partial[orow] = lse;
+    }
   }
 }
 

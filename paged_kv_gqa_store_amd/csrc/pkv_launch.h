@@ -26,6 +26,9 @@ struct DecodeParams {
   const float *rope_cos;     // [rope_rows, D/2] fp32
   const float *rope_sin;
   int rope_rows;
+  // with one split, the merged result written directly (NULL: write partials)
+  uint16_t *out;             // [B, Hq, D] bf16
+  float *lse_out;            // [B, Hq] or NULL
 };
 
 hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,

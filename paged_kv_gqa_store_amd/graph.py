@@ -4,7 +4,8 @@ A one-token step moves too few bytes per kernel to amortise a launch (the
 mini-sglang handbook, "Custom CUDA kernels", section "Exercises", puts a
 per-layer KV write at a fraction of a microsecond and sends it into a graph).
 :class:`StepGraph` records ``n_layers`` x (``kv_store`` -> ``paged_decode_attn``
--> ``decode_merge``) once and replays the whole sequence with one launch.
+-> ``decode_merge``, the last two as one call that is a single kernel when
+there is one split) once and replays the whole sequence with one launch.
 
 The library's entry points are capture-safe by construction: they launch on
 the current stream, never allocate, free, synchronise or memset, and take the
@@ -48,8 +49,10 @@ class StepGraph:
         self.splits = (ops.num_splits(B, Hq, Hkv, max_seq_len, P, total_tokens)
                        if splits is None else splits)
         # The layers run one after another inside the graph, so they share one
-        # partials workspace.
-        self.workspace = ops.workspace(B, Hq, D, self.splits, self.q[0].device)
+        # partials workspace (not needed with one split: the attention then
+        # writes the merged output itself).
+        self.workspace = (ops.workspace(B, Hq, D, self.splits, self.q[0].device)
+                          if self.splits > 1 else (None, None))
         self.outputs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=self.q[0].device)
                         for _ in range(n)]
         self.graph = torch.cuda.CUDAGraph()
@@ -68,9 +71,9 @@ class StepGraph:
         o_p, l_p = self.workspace
         for layer, (k_pool, v_pool) in enumerate(self.pools):
             ops.kv_store(k_pool, v_pool, self.k_new[layer], self.v_new[layer], self.slot_mapping)
-            ops.paged_decode_attn(self.q[layer], k_pool, v_pool, self.page_table, self.seq_lens,
-                                  self.max_seq_len, self.splits, o_partial=o_p, lse_partial=l_p)
-            ops.decode_merge(o_p, l_p, out=self.outputs[layer])
+            ops.paged_decode_attn_merged(self.q[layer], k_pool, v_pool, self.page_table, self.seq_lens,
+                                         self.max_seq_len, self.splits, out=self.outputs[layer],
+                                         o_partial=o_p, lse_partial=l_p)
 
     def replay(self) -> list:
         """Run every captured layer on the current stream; returns ``outputs``."""

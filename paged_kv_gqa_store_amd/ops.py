@@ -275,6 +275,55 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
     return o_partial, lse_partial
 
 
+def paged_decode_attn_merged(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
+                             splits: int | None = None, scale: float | None = None, out=None,
+                             lse_out=None, want_lse: bool = False, o_partial=None, lse_partial=None,
+                             total_tokens: int = -1):
+    """Attention and merge in one call (``pkv_paged_decode_attn_merged``):
+    bf16 ``[B,Hq,D]`` (and fp32 lse ``[B,Hq]``), the same bits as
+    :func:`paged_decode_attn` followed by :func:`decode_merge`.  With one split
+    a single kernel writes the output and no partials are used; with more, the
+    partials (allocated here unless given) feed a second launch."""
+    _on_gpu(q, k_pool, v_pool, page_table, seq_lens)
+    _require(q.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
+             "q and the pools must be bfloat16")
+    _require(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [B,Hq,D]")
+    _require(k_pool.dim() == 4 and k_pool.is_contiguous() and v_pool.is_contiguous()
+             and v_pool.shape == k_pool.shape, "pools must be contiguous [num_pages,P,Hkv,D]")
+    _require(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous(),
+             "page_table must be contiguous int32 [B,max_pages]")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens must be int32")
+    B, Hq, D = q.shape
+    num_pages, P, Hkv, D2 = k_pool.shape
+    _require(D2 == D and page_table.shape[0] == B and seq_lens.shape == (B,), "inconsistent shapes")
+    S = num_splits(B, Hq, Hkv, max_seq_len, P, total_tokens) if splits is None else splits
+    if S > 1 and (o_partial is None or lse_partial is None):
+        o_partial, lse_partial = workspace(B, Hq, D, S, q.device)
+    if o_partial is not None:
+        _require(o_partial.shape == (B, Hq, S, D) and o_partial.dtype == torch.float32
+                 and o_partial.is_contiguous(), "o_partial must be contiguous fp32 [B,Hq,S,D]")
+    if lse_partial is not None:
+        _require(lse_partial.shape == (B, Hq, S) and lse_partial.dtype == torch.float32
+                 and lse_partial.is_contiguous(), "lse_partial must be contiguous fp32 [B,Hq,S]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _require(out.shape == (B, Hq, D) and out.dtype == torch.bfloat16 and out.is_contiguous(),
+             "out must be contiguous bf16 [B,Hq,D]")
+    if want_lse and lse_out is None:
+        lse_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse_out is not None:
+        _require(lse_out.shape == (B, Hq) and lse_out.dtype == torch.float32 and lse_out.is_contiguous(),
+                 "lse_out must be contiguous fp32 [B,Hq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = lib().pkv_paged_decode_attn_merged(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(), seq_lens.data_ptr(),
+        B, Hq, Hkv, D, P, num_pages, page_table.shape[1], max_seq_len, S, scale,
+        ptr(o_partial), ptr(lse_partial), out.data_ptr(), ptr(lse_out), _stream(q))
+    check(st, "pkv_paged_decode_attn_merged")
+    return (out, lse_out) if (want_lse or lse_out is not None) else out
+
+
 def decode_merge(o_partial, lse_partial, out=None, lse_out=None, want_lse: bool = False):
     """Log-sum-exp merge of the split partials -> bf16 ``[B,Hq,D]`` (and fp32 lse ``[B,Hq]``)."""
     _on_gpu(o_partial, lse_partial)
@@ -301,10 +350,11 @@ def decode_merge(o_partial, lse_partial, out=None, lse_out=None, want_lse: bool 
 def decode_step(q, k_new, v_new, k_pool, v_pool, page_table, seq_lens, slot_mapping,
                 max_seq_len: int, splits: int | None = None, out=None, ws=None,
                 want_lse: bool = False, total_tokens: int = -1):
-    """One decode step: store the new rows, split-KV attention, merge."""
+    """One decode step: store the new rows, then split-KV attention and merge
+    (one launch when there is one split)."""
     kv_store(k_pool, v_pool, k_new, v_new, slot_mapping)
-    o_p, l_p = paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits,
-                                 o_partial=None if ws is None else ws[0],
-                                 lse_partial=None if ws is None else ws[1],
-                                 total_tokens=total_tokens)
-    return decode_merge(o_p, l_p, out=out, want_lse=want_lse)
+    return paged_decode_attn_merged(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits,
+                                    out=out, want_lse=want_lse,
+                                    o_partial=None if ws is None else ws[0],
+                                    lse_partial=None if ws is None else ws[1],
+                                    total_tokens=total_tokens)

@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                                          "pkv_num_splits", "pkv_split_chunk", "pkv_status_str",
                                          "pkv_indexing", "pkv_kv_store_rope",
                                          "pkv_paged_decode_attn_rope", "pkv_prefill_plan",
-                                         "pkv_paged_prefill_attn"])
+                                         "pkv_paged_prefill_attn", "pkv_paged_decode_attn_merged"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -163,6 +163,31 @@ def test_attention_validation(lib):
     assert _attn(lib, scale=0.0) == SHAPE
     assert _attn(lib, q=ctypes.c_void_p(258)) == ALIGN
     assert _attn(lib, k=ctypes.c_void_p(264)) == ALIGN
+
+
+def _merged(lib, out=ctypes.c_void_p(256), lse_out=None, **kw):
+    p = ctypes.c_void_p(256)
+    a = dict(q=p, k=p, v=p, pt=p, sl=p, B=2, Hq=8, Hkv=2, D=128, P=16, pages=10, mp=4, L=64, S=2,
+             scale=0.088, o=p, lse=p)
+    a.update(kw)
+    return lib.pkv_paged_decode_attn_merged(a["q"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["Hq"],
+                                            a["Hkv"], a["D"], a["P"], a["pages"], a["mp"], a["L"], a["S"],
+                                            a["scale"], a["o"], a["lse"], out, lse_out, None)
+
+
+def test_merged_attention_validation(lib):
+    # the attention's checks, then the output's; nothing launches on an error
+    assert _merged(lib, B=0) == OK
+    assert _merged(lib, q=None) == NULL
+    assert _merged(lib, D=96) == UNSUP
+    assert _merged(lib, S=0) == SHAPE
+    assert _merged(lib, out=None) == NULL
+    assert _merged(lib, out=ctypes.c_void_p(258)) == ALIGN
+    assert _merged(lib, o=None) == NULL            # several splits need the partials
+    assert _merged(lib, lse=None) == NULL
+    assert _merged(lib, o=ctypes.c_void_p(260)) == ALIGN
+    assert _merged(lib, S=1, o=None, lse=None, out=None) == NULL    # one split: only out is needed
+    assert _merged(lib, S=1, o=None, lse=None, out=ctypes.c_void_p(264)) == ALIGN
 
 
 def test_merge_validation(lib):
