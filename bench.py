@@ -39,8 +39,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, published
 # sources when the counters were taken: any edit to them voids the figure.
 COUNTED_TRAFFIC = {
     "workload": "llama3_8b_decode",
-    "sources_sha256": "ff9789c560a208b60b7128cff5f8d3189311ab3701c8ad0bcb67c050a3265fa6",
-    "read_bytes": 537586655,    # FETCH_SIZE 262505.5 KiB x (1 GiB / 524312.0 KiB)
+    "sources_sha256": "13ee5400316191b9cb2d4e8cf8ac2305e8f74bc83f9fd65966846dc5dacc3d23",
+    "read_bytes": 537570622,    # FETCH_SIZE 262500.9 KiB x (1 GiB / 524318.4 KiB)
     "write_bytes": 532480,      # WRITE_SIZE 520.0 KiB x (1 GiB / 1048576.0 KiB)
 }
 KERNEL_SOURCES = ["pkv_decode_mfma.hip", "pkv_device.h", "pkv_launch.h"]
