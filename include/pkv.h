@@ -11,6 +11,7 @@
  *   pkv_paged_decode_attn split-KV attention through the page table -> partials
  *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
  *   pkv_paged_decode_attn_merged  the attention and the merge in one call
+ *   pkv_decode_step       store, attention and merge in one call (one kernel at S = 1)
  *   pkv_num_splits        split-count heuristic (host only)
  *   pkv_split_chunk       positions per split for a split count (host only)
  *   pkv_status_str        text of a status code
@@ -275,6 +276,40 @@ pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const
                                         int32_t num_splits, float scale, float *o_partial,
                                         float *lse_partial, void *out, float *lse_out,
                                         void *stream);
+
+/*
+ * pkv_decode_step -- one whole decode step: pkv_kv_store of one new row per
+ * sequence, then pkv_paged_decode_attn_merged, in one call, with the same
+ * pools, output and lse bit for bit.
+ *
+ * Follows the passages of those calls (mini-sglang handbook, "Custom CUDA
+ * kernels", "Moving whole rows by index"; AstrAI "CUDA Kernels", "Q
+ * Scheduling and KV Addressing"; cuDNN frontend "CSA Fused Compressor",
+ * "ratio=128").  The store is fused into the attention kernel: the workgroup
+ * of head g whose split holds position seq_lens[b] - 1 copies head g of row b
+ * of k_new / v_new to pool slot slot_mapping[b], and the attention takes that
+ * position from the new row itself.  With num_splits == 1 the whole step is
+ * one kernel and o_partial / lse_partial may be NULL; otherwise the merge
+ * runs as a second launch.
+ *   k_new, v_new   device bf16 [B, new_row_stride], 16-byte aligned; row b is
+ *                  the new token of sequence b, Hkv*D values per row
+ *   new_row_stride elements between rows, >= Hkv*D, a multiple of 8
+ *   slot_mapping   device int32 [B]; slots outside [0, num_pages*page_size)
+ *                  are not written (as pkv_kv_store)
+ *   k_pool, v_pool written (one row per sequence); other arguments as
+ *                  pkv_paged_decode_attn_merged
+ * Preconditions (device, as in the unfused step): seq_lens[b] >= 1 counts the
+ * new token, and slot_mapping[b] is the slot of its position seq_lens[b] - 1
+ * (page_table[b][(L-1)/P]*P + (L-1)%P); the slots are distinct.
+ * Always runs the matrix-core attention kernel.
+ */
+pkv_status pkv_decode_step(const void *q, const void *k_new, const void *v_new,
+                           int64_t new_row_stride, const int32_t *slot_mapping, void *k_pool,
+                           void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                           int32_t num_pages, int32_t max_pages_per_seq, int32_t max_seq_len,
+                           int32_t num_splits, float scale, float *o_partial, float *lse_partial,
+                           void *out, float *lse_out, void *stream);
 
 /*
  * pkv_num_splits -- split count for a batch (host only, no GPU call).

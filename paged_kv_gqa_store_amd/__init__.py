@@ -8,7 +8,8 @@ One decode step is three hand-written HIP kernels behind a C ABI
 * ``decode_merge``       log-sum-exp merge of the split partials;
 
 (``paged_decode_attn_merged`` runs the last two as one call: a single kernel
-when there is one split),
+when there is one split; ``decode_step_fused`` runs all three as one call,
+the store fused into the attention kernel),
 
 plus ``paged_prefill_attn`` (packed multi-token queries over the same pool,
 with the ``prefill_plan`` work map), ``kv_store_rope`` (the store with K rotated by a rotary embedding on the
@@ -23,7 +24,7 @@ every op raises ``RuntimeError`` if ``libpkv.so`` is missing: there is no
 fallback implementation.
 """
 from .ops import (  # noqa: F401
-    PrefillPlan, decode_merge, decode_step, indexing, kv_store, kv_store_rope, num_splits,
+    PrefillPlan, decode_merge, decode_step, decode_step_fused, indexing, kv_store, kv_store_rope, num_splits,
     paged_decode_attn, paged_decode_attn_merged, paged_prefill_attn, prefill_plan, split_chunk,
     workspace,
 )

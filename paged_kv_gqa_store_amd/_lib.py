@@ -26,6 +26,8 @@ SIGNATURES = [
     ("pkv_paged_decode_attn", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                      _i32, _i32, _f32, _p, _p, _p]),
     ("pkv_decode_merge", _i32, [_p, _p, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    ("pkv_decode_step", _i32, [_p, _p, _p, _i64, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p]),
     ("pkv_paged_decode_attn_merged", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f32, _p, _p, _p, _p, _p]),
     ("pkv_prefill_plan", _i32, [_p, _i32, _p, _p, _p, _i32]),

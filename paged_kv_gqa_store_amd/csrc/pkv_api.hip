@@ -353,6 +353,42 @@ pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+pkv_status pkv_decode_step(const void *q, const void *k_new, const void *v_new,
+                           int64_t new_row_stride, const int32_t *slot_mapping, void *k_pool,
+                           void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                           int32_t num_pages, int32_t max_pages_per_seq, int32_t max_seq_len,
+                           int32_t num_splits, float scale, float *o_partial, float *lse_partial,
+                           void *out, float *lse_out, void *stream) {
+  pkv::DecodeParams p;
+  const bool one = num_splits == 1;
+  pkv_status st = attention_params(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D,
+                                   page_size, num_pages, max_pages_per_seq, max_seq_len,
+                                   num_splits, scale, o_partial, lse_partial, p, !one);
+  if (st != PKV_OK || p.B == 0) return st;
+  if (!out || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
+  if (new_row_stride < int64_t(Hkv) * D) return PKV_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(k_new) || !aligned16(v_new) || (new_row_stride * 2) % 16)
+    return PKV_ERR_ALIGN;
+  if (int64_t(B) * Hq > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
+  if (!one && !aligned16(o_partial)) return PKV_ERR_ALIGN;
+  p.k_new = static_cast<const uint16_t *>(k_new);
+  p.v_new = static_cast<const uint16_t *>(v_new);
+  p.new_stride = new_row_stride;
+  p.slots = slot_mapping;
+  p.num_slots = int64_t(num_pages) * page_size;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (one) {
+    p.out = static_cast<uint16_t *>(out);
+    p.lse_out = lse_out;
+    return pkv::launch_paged_decode_mfma(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  }
+  if (pkv::launch_paged_decode_mfma(p, s) != hipSuccess) return PKV_ERR_HIP;
+  const hipError_t e = pkv::launch_decode_merge(o_partial, lse_partial, B * Hq, D, num_splits,
+                                                static_cast<uint16_t *>(out), lse_out, s);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 pkv_status pkv_decode_merge(const float *o_partial, const float *lse_partial, int32_t B,
                             int32_t Hq, int32_t D, int32_t num_splits, void *out, float *lse_out,
                             void *stream) {

@@ -93,8 +93,10 @@ __device__ __forceinline__ void pin_issue_order() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int G, bool kPageTile, int NBUF, int kWaves, bool kRope>
+// kMode: 0 plain; 1 q rotated in the prologue; 2 the step's kv_store fused in
+template <int D, int G, bool kPageTile, int NBUF, int kWaves, int kMode>
 __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodeParams p) {
+  constexpr bool kRope = kMode == 1, kFuse = kMode == 2;
   constexpr int KS = D / 32;      // MFMA k-steps per tile = V loads per lane per tile
   constexpr int LPV = D / 8;      // lanes per token in the V layout
   constexpr int TPV = 64 / LPV;   // tokens per V load instruction
@@ -133,6 +135,24 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.max_pages << log2P);
   const int t1 = min(t0 + p.chunk, L);
+  if constexpr (kFuse) {
+    // The step's store, fused: the split holding position L - 1 (split 0 for
+    // an empty sequence) copies head g of the new K/V row to its pool slot,
+    // 16 bytes per lane (the store's contract: an index outside the pool is
+    // not written).  The attention takes position L - 1 from the new row
+    // itself, so no ordering with these writes is needed.
+    const int sw = L > 0 ? min((L - 1) / p.chunk, p.num_splits - 1) : 0;
+    constexpr int LPR = D / 8;
+    if (s == sw && wave == 0 && lane < 2 * LPR) {
+      const int64_t slot = p.slots[b];
+      if (slot >= 0 && slot < p.num_slots) {
+        const size_t c = size_t(g) * D + 8 * (lane % LPR);
+        const uint16_t *src = (lane < LPR ? p.k_new : p.v_new) + size_t(b) * p.new_stride + c;
+        uint16_t *dst = const_cast<uint16_t *>(lane < LPR ? p.k_pool : p.v_pool) + size_t(slot) * p.Hkv * D + c;
+        *reinterpret_cast<u32x4 *>(dst) = ld16(src);
+      }
+    }
+  }
 
   // q rows of the group as the MFMA A operand: lane = head (lane & 15), dims 32j + 8(lane >> 4)
   const int qh = lane & 15, qk = lane >> 4;
@@ -186,6 +206,12 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   const uint16_t *vbase = p.v_pool + size_t(g) * D + 8 * (lane % LPV);
   const uint16_t *qrow = p.q + (size_t(b) * p.Hq + size_t(g) * G) * D + 8 * (lane % LPV);
   const int vt = lane / LPV;
+  // fused store: position L - 1 is read from the new rows
+  [[maybe_unused]] const uint16_t *knew = nullptr, *vnew = nullptr;
+  if constexpr (kFuse) {
+    knew = p.k_new + size_t(b) * p.new_stride + size_t(g) * D + 8 * (lane % LPV);
+    vnew = p.v_new + size_t(b) * p.new_stride + size_t(g) * D + 8 * (lane % LPV);
+  }
 
   struct Regs { u32x4 k[KS]; u32x4 v[KS]; int pid; };
 
@@ -223,9 +249,16 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
         const size_t page_row = size_t(pid) << log2P;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-          const size_t row = page_row + (min(tb + TPV * i + vt, last) & pmask);
-          rg.k[i] = ld16_stream(kb + row * rs);
-          rg.v[i] = ld16_stream(vb + row * rs);
+          const int tv = min(tb + TPV * i + vt, last);
+          const size_t row = page_row + (tv & pmask);
+          const uint16_t *ka = kb + row * rs, *va = vb + row * rs;
+          if constexpr (kFuse) {
+            const bool fresh = real && tv == L - 1;
+            ka = fresh ? knew : ka;
+            va = fresh ? vnew : va;
+          }
+          rg.k[i] = ld16_stream(ka);
+          rg.v[i] = ld16_stream(va);
         }
       } else {
         rg.pid = sm_pid[(min(tb + (lane & 15), last) >> log2P) - pga];   // page of this lane's score token
@@ -235,8 +268,14 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
           const int rv = sm_pid[(tv >> log2P) - pga];
           const int pv = unsigned(rv) < unsigned(p.num_pages) ? rv : 0;
           const size_t row = (size_t(pv) << log2P) + (tv & pmask);
-          rg.k[i] = ld16_stream(kb + row * rs);
-          rg.v[i] = ld16_stream(vb + row * rs);
+          const uint16_t *ka = kb + row * rs, *va = vb + row * rs;
+          if constexpr (kFuse) {
+            const bool fresh = real && tv == L - 1;
+            ka = fresh ? knew : ka;
+            va = fresh ? vnew : va;
+          }
+          rg.k[i] = ld16_stream(ka);
+          rg.v[i] = ld16_stream(va);
         }
       }
     };
@@ -406,16 +445,16 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   }
 }
 
-template <int D, int G, bool kRope>
+template <int D, int G, int kMode>
 hipError_t launch_mfma(const DecodeParams &p, hipStream_t stream) {
   constexpr int kWaves = 4;
   const dim3 grid{unsigned(p.num_splits * p.Hkv * p.B)}, block{kWaves * 64};
   constexpr int NBUF = D == 128 ? 3 : 4;
   if (p.page_log2 >= 4)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, kWaves, kRope>), grid, block, 0,
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, kWaves, kMode>), grid, block, 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false, NBUF, kWaves, kRope>), grid, block, 0,
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, false, NBUF, kWaves, kMode>), grid, block, 0,
                        stream, p);
   return hipGetLastError();
 }
@@ -425,7 +464,8 @@ hipError_t launch_mfma(const DecodeParams &p, hipStream_t stream) {
 hipError_t launch_paged_decode_mfma(const DecodeParams &p, hipStream_t stream) {
 #define PKV_CASE(DD, GG)                                                        \
   if (p.D == DD && p.G == GG)                                                   \
-    return p.q_pos ? launch_mfma<DD, GG, true>(p, stream) : launch_mfma<DD, GG, false>(p, stream);
+    return p.q_pos ? launch_mfma<DD, GG, 1>(p, stream)                        \
+                   : (p.k_new ? launch_mfma<DD, GG, 2>(p, stream) : launch_mfma<DD, GG, 0>(p, stream));
   PKV_CASE(64, 1) PKV_CASE(64, 2) PKV_CASE(64, 4) PKV_CASE(64, 8)
   PKV_CASE(128, 1) PKV_CASE(128, 2) PKV_CASE(128, 4) PKV_CASE(128, 8)
 #undef PKV_CASE

@@ -29,6 +29,13 @@ struct DecodeParams {
   // with one split, the merged result written directly (NULL: write partials)
   uint16_t *out;             // [B, Hq, D] bf16
   float *lse_out;            // [B, Hq] or NULL
+  // the step's kv_store fused in (k_new NULL when not): row b of k_new / v_new
+  // goes to pool slot slots[b], and is position seq_lens[b] - 1
+  const uint16_t *k_new;
+  const uint16_t *v_new;
+  int64_t new_stride;        // elements between rows of k_new / v_new
+  const int32_t *slots;      // [B]
+  int64_t num_slots;         // num_pages * page_size
 };
 
 hipError_t launch_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_stride_b,

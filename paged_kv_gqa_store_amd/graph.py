@@ -29,13 +29,17 @@ class StepGraph:
     sequences).  All of them are static: refill them in place between
     replays.  ``max_seq_len`` and the split count are fixed at capture, so a
     server keeps one graph per length bucket.  ``outputs[l]`` is layer l's
-    ``[B, Hq, D]`` bf16 result, overwritten by every replay.  Construction
+    ``[B, Hq, D]`` bf16 result, overwritten by every replay.  With ``fused``
+    (the default) each layer is one ``pkv_decode_step`` call, the store fused
+    into the attention kernel; that needs one new row per sequence and
+    ``slot_mapping[b]`` the slot of position ``seq_lens[b] - 1``.  Construction
     runs the layers once eagerly before capturing them (the same work a
     replay does: the new rows are stored, the outputs computed).
     """
 
     def __init__(self, pools, q, k_new, v_new, page_table, seq_lens, slot_mapping,
-                 max_seq_len: int, splits: int | None = None, total_tokens: int = -1):
+                 max_seq_len: int, splits: int | None = None, total_tokens: int = -1,
+                 fused: bool = True):
         n = len(pools)
         per_layer = lambda x: list(x) if isinstance(x, (list, tuple)) else [x] * n
         self.pools = list(pools)
@@ -43,6 +47,7 @@ class StepGraph:
         if not (len(self.q) == len(self.k_new) == len(self.v_new) == n) or n == 0:
             raise RuntimeError("one q / k_new / v_new per layer (or one shared)")
         self.page_table, self.seq_lens, self.slot_mapping = page_table, seq_lens, slot_mapping
+        self.fused = fused
         B, Hq, D = self.q[0].shape
         P, Hkv = self.pools[0][0].shape[1], self.pools[0][0].shape[2]
         self.max_seq_len = max_seq_len
@@ -70,6 +75,11 @@ class StepGraph:
     def _record(self):
         o_p, l_p = self.workspace
         for layer, (k_pool, v_pool) in enumerate(self.pools):
+            if self.fused:
+                ops.decode_step_fused(self.q[layer], self.k_new[layer], self.v_new[layer], k_pool, v_pool,
+                                      self.page_table, self.seq_lens, self.slot_mapping, self.max_seq_len,
+                                      self.splits, out=self.outputs[layer], o_partial=o_p, lse_partial=l_p)
+                continue
             ops.kv_store(k_pool, v_pool, self.k_new[layer], self.v_new[layer], self.slot_mapping)
             ops.paged_decode_attn_merged(self.q[layer], k_pool, v_pool, self.page_table, self.seq_lens,
                                          self.max_seq_len, self.splits, out=self.outputs[layer],

@@ -275,15 +275,10 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
     return o_partial, lse_partial
 
 
-def paged_decode_attn_merged(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
-                             splits: int | None = None, scale: float | None = None, out=None,
-                             lse_out=None, want_lse: bool = False, o_partial=None, lse_partial=None,
-                             total_tokens: int = -1):
-    """Attention and merge in one call (``pkv_paged_decode_attn_merged``):
-    bf16 ``[B,Hq,D]`` (and fp32 lse ``[B,Hq]``), the same bits as
-    :func:`paged_decode_attn` followed by :func:`decode_merge`.  With one split
-    a single kernel writes the output and no partials are used; with more, the
-    partials (allocated here unless given) feed a second launch."""
+def _merged_args(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits, scale, out, lse_out,
+                 want_lse, o_partial, lse_partial, total_tokens):
+    """Checks shared by the calls that end in the merged bf16 output; returns
+    the marshalled attention arguments, out and lse_out."""
     _on_gpu(q, k_pool, v_pool, page_table, seq_lens)
     _require(q.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
              "q and the pools must be bfloat16")
@@ -316,11 +311,51 @@ def paged_decode_attn_merged(q, k_pool, v_pool, page_table, seq_lens, max_seq_le
                  "lse_out must be contiguous fp32 [B,Hq]")
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ptr = lambda t: t.data_ptr() if t is not None else None
-    st = lib().pkv_paged_decode_attn_merged(
-        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(), seq_lens.data_ptr(),
-        B, Hq, Hkv, D, P, num_pages, page_table.shape[1], max_seq_len, S, scale,
-        ptr(o_partial), ptr(lse_partial), out.data_ptr(), ptr(lse_out), _stream(q))
+    tail = (page_table.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, D, P, num_pages, page_table.shape[1],
+            max_seq_len, S, scale, ptr(o_partial), ptr(lse_partial), out.data_ptr(), ptr(lse_out))
+    return tail, out, lse_out
+
+
+def paged_decode_attn_merged(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
+                             splits: int | None = None, scale: float | None = None, out=None,
+                             lse_out=None, want_lse: bool = False, o_partial=None, lse_partial=None,
+                             total_tokens: int = -1):
+    """Attention and merge in one call (``pkv_paged_decode_attn_merged``):
+    bf16 ``[B,Hq,D]`` (and fp32 lse ``[B,Hq]``), the same bits as
+    :func:`paged_decode_attn` followed by :func:`decode_merge`.  With one split
+    a single kernel writes the output and no partials are used; with more, the
+    partials (allocated here unless given) feed a second launch."""
+    tail, out, lse_out = _merged_args(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits, scale,
+                                      out, lse_out, want_lse, o_partial, lse_partial, total_tokens)
+    st = lib().pkv_paged_decode_attn_merged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), *tail,
+                                            _stream(q))
     check(st, "pkv_paged_decode_attn_merged")
+    return (out, lse_out) if (want_lse or lse_out is not None) else out
+
+
+def decode_step_fused(q, k_new, v_new, k_pool, v_pool, page_table, seq_lens, slot_mapping,
+                      max_seq_len: int, splits: int | None = None, scale: float | None = None, out=None,
+                      lse_out=None, want_lse: bool = False, o_partial=None, lse_partial=None,
+                      total_tokens: int = -1):
+    """One decode step in one call (``pkv_decode_step``): the store of one new
+    row per sequence fused into the attention kernel, then the merge (no
+    second launch with one split).  Same pools, output and lse, bit for bit, as
+    :func:`kv_store` then :func:`paged_decode_attn_merged`, provided
+    ``slot_mapping[b]`` is the slot of position ``seq_lens[b] - 1``.
+    ``k_new``/``v_new``: ``[B, Hkv, D]`` or ``[B, Hkv*D]`` bf16, rows contiguous."""
+    _on_gpu(k_new, v_new, slot_mapping)
+    kn, vn = _rows(k_new, "k_new", False), _rows(v_new, "v_new", False)
+    _require(kn.shape == vn.shape and kn.stride() == vn.stride(), "k_new and v_new must match")
+    _require(kn.dtype == torch.bfloat16 and vn.dtype == torch.bfloat16, "new rows must be bfloat16")
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.is_contiguous()
+             and slot_mapping.shape == (q.shape[0],), "slot_mapping must be contiguous int32 [B]")
+    _require(kn.shape[0] == q.shape[0] and kn.shape[1] == k_pool.shape[2] * k_pool.shape[3],
+             "one new row of Hkv*D values per sequence")
+    tail, out, lse_out = _merged_args(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits, scale,
+                                      out, lse_out, want_lse, o_partial, lse_partial, total_tokens)
+    st = lib().pkv_decode_step(q.data_ptr(), kn.data_ptr(), vn.data_ptr(), kn.stride(0),
+                               slot_mapping.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), *tail, _stream(q))
+    check(st, "pkv_decode_step")
     return (out, lse_out) if (want_lse or lse_out is not None) else out
 
 

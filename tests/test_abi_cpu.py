@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
                                          "pkv_num_splits", "pkv_split_chunk", "pkv_status_str",
                                          "pkv_indexing", "pkv_kv_store_rope",
                                          "pkv_paged_decode_attn_rope", "pkv_prefill_plan",
-                                         "pkv_paged_prefill_attn", "pkv_paged_decode_attn_merged"])
+                                         "pkv_paged_prefill_attn", "pkv_paged_decode_attn_merged",
+                                         "pkv_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -188,6 +189,28 @@ def test_merged_attention_validation(lib):
     assert _merged(lib, o=ctypes.c_void_p(260)) == ALIGN
     assert _merged(lib, S=1, o=None, lse=None, out=None) == NULL    # one split: only out is needed
     assert _merged(lib, S=1, o=None, lse=None, out=ctypes.c_void_p(264)) == ALIGN
+
+
+def _step(lib, kn=ctypes.c_void_p(256), stride=256, slots=ctypes.c_void_p(256), out=ctypes.c_void_p(256), **kw):
+    p = ctypes.c_void_p(256)
+    a = dict(q=p, k=p, v=p, pt=p, sl=p, B=2, Hq=8, Hkv=2, D=128, P=16, pages=10, mp=4, L=64, S=1,
+             scale=0.088, o=None, lse=None)
+    a.update(kw)
+    return lib.pkv_decode_step(a["q"], kn, p, stride, slots, a["k"], a["v"], a["pt"], a["sl"], a["B"], a["Hq"],
+                               a["Hkv"], a["D"], a["P"], a["pages"], a["mp"], a["L"], a["S"], a["scale"],
+                               a["o"], a["lse"], out, None, None)
+
+
+def test_decode_step_validation(lib):
+    assert _step(lib, B=0) == OK
+    assert _step(lib, kn=None) == NULL
+    assert _step(lib, slots=None) == NULL
+    assert _step(lib, out=None) == NULL
+    assert _step(lib, stride=255) == SHAPE         # shorter than a row of Hkv*D
+    assert _step(lib, stride=260) == ALIGN         # rows not 16-byte aligned
+    assert _step(lib, kn=ctypes.c_void_p(264)) == ALIGN
+    assert _step(lib, S=2) == NULL                 # several splits need the partials
+    assert _step(lib, D=96) == UNSUP
 
 
 def test_merge_validation(lib):

@@ -36,18 +36,19 @@ def _layer_inputs(inp, n_layers, dev):
     return layers
 
 
-@pytest.mark.parametrize("cid,n_layers,splits", [(1, 3, 2), (3, 2, None)])
-def test_replays_equal_the_eager_step(gpu_device, cid, n_layers, splits):
+@pytest.mark.parametrize("cid,n_layers,splits,fused", [(1, 3, 2, True), (3, 2, None, True), (2, 2, 1, True),
+                                                      (1, 2, 2, False), (2, 2, 1, False)])
+def test_replays_equal_the_eager_step(gpu_device, cid, n_layers, splits, fused):
     base = W.make_inputs(W.CONFIGS[cid])
     layers = _layer_inputs(base, n_layers, gpu_device)
     total = int(base.seq_lens.sum())
-    print(f"graph step cfg {cid}, {n_layers} layers, splits {splits}", flush=True)
+    print(f"graph step cfg {cid}, {n_layers} layers, splits {splits}, fused {fused}", flush=True)
     # graph side: one set of device tensors per layer (page table, lengths, slots shared)
     dsteps = [DeviceStep(li, gpu_device) for li in layers]
     shared = dsteps[0]
     g = StepGraph([(d.k_pool, d.v_pool) for d in dsteps], [d.q for d in dsteps],
                   [d.k_new for d in dsteps], [d.v_new for d in dsteps], shared.page_table,
-                  shared.seq_lens, shared.slot_mapping, base.max_seq_len, splits, total)
+                  shared.seq_lens, shared.slot_mapping, base.max_seq_len, splits, total, fused=fused)
     # eager side: fresh copies of the same inputs
     esteps = [DeviceStep(li, gpu_device) for li in layers]
     eager = [e.step(g.splits)[0] for e in esteps]
