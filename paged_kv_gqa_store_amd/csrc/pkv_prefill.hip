@@ -20,10 +20,12 @@
 //                  rounded to bf16 for the matrix core; the accumulators and
 //                  the softmax statistics stay fp32.
 // With two or more q heads per kv head a wave owns 32 query rows of one head
-// and both products use v_mfma_f32_32x32x16_bf16, which sustains about twice
-// the rate of the 16x16x32 form on this chip; with one q head per kv head a
-// workgroup's 64 rows are spread over its 4 waves, 16 each, on the 16x16x32
-// form.
+// and both products use v_mfma_f32_32x32x16_bf16, which sustained about
+// twice the rate of the 16x16x32 form in a microbenchmark on this chip
+// (independent accumulation chains); with four or more q heads per kv head
+// the workgroup has 8 waves (4 heads x 64 rows), so one K/V tile in LDS
+// serves twice the rows.  With one q head per kv head a workgroup's 64 rows
+// are spread over its 4 waves, 16 each, on the 16x16x32 form.
 // K and V tiles of 64 tokens move from the pool into LDS with direct loads
 // (global_load_lds_dwordx4: 16 bytes per lane, no registers, no staging
 // code), double-buffered, so one barrier per tile separates the loads of tile
@@ -50,7 +52,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQTile = PKV_PREFILL_TILE_ROWS;   // query rows per host tile
 constexpr int kKT = 64;                         // tokens per K/V tile
-constexpr int kThreads = 256;                   // 4 waves
+constexpr int kThreads = 256;                   // 4 waves (the 16x16x32 kernel)
 constexpr float kLazy = 8.f;                    // lazy rescale threshold (log2 units)
 
 #define PKV_LDS __attribute__((address_space(3)))
@@ -135,16 +137,18 @@ __device__ __forceinline__ bool locate(const PrefillParams &p, Slice &w) {
   return true;
 }
 
-// Direct loads of one 64-token K/V tile into a pair of LDS buffers: load n of
-// a wave fills tile rows 16 * wave + n * RPI + lrow (lrow = lane / LPR); the
-// lane's 16 bytes land at physical chunk lane % LPR, so it fetches the
-// logical chunk that swz maps there.
-template <int D>
+// Direct loads of one 64-token K/V tile into a pair of LDS buffers by the W
+// waves of a workgroup: load n of a wave fills tile rows RWV * wave + n * RPI
+// + lrow (RWV = 64 / W, lrow = lane / LPR); the lane's 16 bytes land at
+// physical chunk lane % LPR, so it fetches the logical chunk that swz maps
+// there.
+template <int D, int W = 4>
 struct TileLoader {
   static constexpr int PITCH = 2 * D;        // bytes per K/V row in LDS
   static constexpr int LPR = D / 8;          // lanes (16-byte chunks) per row
   static constexpr int RPI = 64 / LPR;       // rows per direct load (64 lanes)
-  static constexpr int NI = kKT / (4 * RPI); // direct loads per wave, tile and tensor
+  static constexpr int RWV = kKT / W;        // tile rows loaded by each wave
+  static constexpr int NI = RWV / RPI;       // direct loads per wave, tile and tensor
 
   const PrefillParams &p;
   const int32_t *pt;                         // the request's page-table row
@@ -160,8 +164,8 @@ struct TileLoader {
       : p(p_), wave(wave_), g(w.g), kv_end(w.kv_end) {
     log2P = p.page_log2;
     pmask = (1 << log2P) - 1;
-    // A wave loads 16 consecutive positions per tile; with pages of 16 or
-    // more tokens they share one page, whose id is wave-uniform and read a
+    // A wave loads RWV <= 16 consecutive positions per tile; with pages of 16
+    // or more tokens they share one page, whose id is wave-uniform and read a
     // tile ahead with a scalar load (its own counter, so waiting for it never
     // waits for the direct loads in flight; the page table is read-only here,
     // and the constant address space lets the uniform load be scalar).
@@ -173,25 +177,25 @@ struct TileLoader {
     row_stride = size_t(p.Hkv) * D;
     row_bytes = unsigned(row_stride) * 2u;
 #pragma unroll
-    for (int n = 0; n < NI; ++n) colb[n] = 2 * (g * D + 8 * (pc ^ swz<D>(n * RPI + lrow)));
+    for (int n = 0; n < NI; ++n) colb[n] = 2 * (g * D + 8 * (pc ^ swz<D>((RWV * wave + n * RPI + lrow) & 15)));
   }
 
   __device__ __forceinline__ void fetch_pid(int t0) {
-    const int t = t0 + 16 * wave;
+    const int t = t0 + RWV * wave;
     pid_next = (big_pages && t < kv_end) ? pt_s[t >> log2P] : 0;
   }
 
   __device__ __forceinline__ void issue(int t0, unsigned char *kb, unsigned char *vb) {
     const int pid = __builtin_amdgcn_readfirstlane(pid_next);
     if (big_pages && t0 + kKT <= kv_end && unsigned(pid) < unsigned(p.num_pages)) {
-      // the wave's 16 positions are inside the sequence, in one pool page
-      const unsigned row0 = (unsigned(pid) << log2P) | unsigned((t0 + 16 * wave) & pmask);
+      // the wave's RWV positions are inside the sequence, in one pool page
+      const unsigned row0 = (unsigned(pid) << log2P) | unsigned((t0 + RWV * wave) & pmask);
       const unsigned char *kbytes = reinterpret_cast<const unsigned char *>(p.k_pool);
       const unsigned char *vbytes = reinterpret_cast<const unsigned char *>(p.v_pool);
 #pragma unroll
       for (int n = 0; n < NI; ++n) {
         const uint64_t a = uint64_t(row0 + unsigned(n * RPI + lrow)) * row_bytes + unsigned(colb[n]);
-        const int dst = (16 * wave + n * RPI) * PITCH;
+        const int dst = (RWV * wave + n * RPI) * PITCH;
         __builtin_amdgcn_global_load_lds(const_cast<unsigned char *>(kbytes + a), (PKV_LDS void *)(kb + dst), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(const_cast<unsigned char *>(vbytes + a), (PKV_LDS void *)(vb + dst), 16, 0, 0);
       }
@@ -201,8 +205,8 @@ struct TileLoader {
     // read zeros, a page id outside the pool reads NaN
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
-      const int t = t0 + 16 * wave + n * RPI + lrow;
-      const int c = pc ^ swz<D>(n * RPI + lrow);
+      const int t = t0 + RWV * wave + n * RPI + lrow;
+      const int c = pc ^ swz<D>((RWV * wave + n * RPI + lrow) & 15);
       const int pg = t < kv_end ? pt[t >> log2P] : 0;
       const bool in_pool = t < kv_end && unsigned(pg) < unsigned(p.num_pages);
       const size_t off = ((size_t(in_pool ? pg : 0) << log2P) + (t & pmask)) * row_stride +
@@ -210,7 +214,7 @@ struct TileLoader {
       const u32x4 *alt = kFillRows + (t < kv_end ? 1 : 0);
       const u32x4 *ks = in_pool ? reinterpret_cast<const u32x4 *>(p.k_pool + off) : alt;
       const u32x4 *vs = in_pool ? reinterpret_cast<const u32x4 *>(p.v_pool + off) : alt;
-      const int dst = (16 * wave + n * RPI) * PITCH;
+      const int dst = (RWV * wave + n * RPI) * PITCH;
       __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(ks), (PKV_LDS void *)(kb + dst), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(const_cast<u32x4 *>(vs), (PKV_LDS void *)(vb + dst), 16, 0, 0);
     }
@@ -230,8 +234,8 @@ __device__ __forceinline__ void tile_barrier() {
 // with the buffer pair that the next loads overwrite.  The page id of the tile
 // after next is fetched at the end of a tile, so its latency hides in the
 // barrier's wait.
-template <int D, class Compute>
-__device__ __forceinline__ void tile_loop(TileLoader<D> &ld, int kv_end, unsigned char *k0,
+template <class Loader, class Compute>
+__device__ __forceinline__ void tile_loop(Loader &ld, int kv_end, unsigned char *k0,
                                           unsigned char *v0, unsigned char *k1, unsigned char *v1,
                                           Compute &&compute) {
   const int ntiles = (kv_end + kKT - 1) / kKT;
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void paged_prefill16_kernel(PrefillParams
       }
   };
   TileLoader<D> ld(p, w, wave, lane);
-  tile_loop<D>(ld, kv_end, sm_k0, sm_v0, sm_k1, sm_v1, compute);
+  tile_loop(ld, kv_end, sm_k0, sm_v0, sm_k1, sm_v1, compute);
 
   // row sums over the 4 lane groups, then the output row
   float lsum = l;
@@ -397,13 +401,13 @@ __global__ __launch_bounds__(kThreads) void paged_prefill16_kernel(PrefillParams
 
 // Two or more q heads per kv head: a wave owns 32 query rows of one head, on
 // the 32x32x16 form (lane & 31 = query row; register r of a 32-token block is
-// token 8(r / 4) + 4(lane >> 5) + r % 4).  HB heads per workgroup, 4 / HB
-// waves per head.
-template <int D, int HB>
-__global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams p) {
+// token 8(r / 4) + 4(lane >> 5) + r % 4).  HB heads per workgroup, W / HB
+// waves per head (W = 8 when HB = 4, else 4).
+template <int D, int HB, int W>
+__global__ __launch_bounds__(W * 64) void paged_prefill32_kernel(PrefillParams p) {
   constexpr int KS = D / 16;                 // k-steps of S^T over the head dimension
   constexpr int MB = D / 32;                 // 32-dim blocks of O^T
-  constexpr int WPH = 4 / HB;                // waves per q head
+  constexpr int WPH = W / HB;                // waves per q head
   constexpr int RW = WPH * 32;               // query rows per workgroup and head
   static_assert(kQTile % RW == 0, "row split");
   constexpr int PITCH = TileLoader<D>::PITCH;
@@ -536,8 +540,8 @@ __global__ __launch_bounds__(kThreads) void paged_prefill32_kernel(PrefillParams
         o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(pb[st]), o[i], 0, 0, 0);
       }
   };
-  TileLoader<D> ld(p, w, wave, lane);
-  tile_loop<D>(ld, kv_end, sm_k0, sm_v0, sm_k1, sm_v1, compute);
+  TileLoader<D, W> ld(p, w, wave, lane);
+  tile_loop(ld, kv_end, sm_k0, sm_v0, sm_k1, sm_v1, compute);
 
   const float lsum = sum_xor32(l);
   if (!row_ok) return;
@@ -564,12 +568,12 @@ hipError_t launch16(const PrefillParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int HB>
+template <int D, int HB, int W = 8>
 hipError_t launch32(const PrefillParams &p, hipStream_t stream) {
-  constexpr int CH = kQTile / ((4 / HB) * 32);
+  constexpr int CH = kQTile / ((W / HB) * 32);
   const int hgroups = (p.G + HB - 1) / HB;
-  const dim3 grid{unsigned(p.num_q_tiles * CH * p.Hkv * hgroups)}, block{kThreads};
-  hipLaunchKernelGGL((paged_prefill32_kernel<D, HB>), grid, block, 0, stream, p);
+  const dim3 grid{unsigned(p.num_q_tiles * CH * p.Hkv * hgroups)}, block{W * 64};
+  hipLaunchKernelGGL((paged_prefill32_kernel<D, HB, W>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -584,7 +588,7 @@ hipError_t launch_paged_prefill(const PrefillParams &p, hipStream_t stream) {
     return hipErrorInvalidValue;
   }
 #define PKV_CASE(DD, HH) \
-  if (p.D == DD && HB == HH) return launch32<DD, HH>(p, stream);
+  if (p.D == DD && HB == HH) return launch32<DD, HH, HH == 4 ? 8 : 4>(p, stream);
   PKV_CASE(64, 2) PKV_CASE(64, 4) PKV_CASE(128, 2) PKV_CASE(128, 4)
 #undef PKV_CASE
   return hipErrorInvalidValue;
