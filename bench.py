@@ -137,6 +137,25 @@ def time_graph_launches(fn, n: int) -> float:
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def measure_copy_ceiling(dev, reps: int = 10) -> float:
+    """GB/s of a plain 16-byte-vector device copy of 1 GiB (bytes read + written),
+    the practical ceiling of a read+write move such as kv_store on this machine."""
+    import torch
+    src = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    del src, dst
+    return 2 * (1 << 30) / (ms * 1e-3) / 1e9
+
+
 def measure_extras(args, pkv, W, dev, to_bf16, to_i32) -> dict:
     """Secondary rows of the path, each on its own synthetic workload."""
     import torch
@@ -310,6 +329,9 @@ def main():
     store_gbps = store_b / (bulk_us * 1e-6) / 1e9
     log(f"[bench] kv_store bulk fill: {bslots.shape[0]} rows, {store_b / 1e6:.1f} MB in {bulk_us:.1f} us = "
         f"{store_gbps:.0f} GB/s ({store_gbps / PEAK_HBM_GBPS:.1%})")
+    copy_gbps = measure_copy_ceiling(dev)
+    log(f"[bench] device copy on this box (practical ceiling of a read+write move): {copy_gbps:.0f} GB/s "
+        f"({copy_gbps / PEAK_HBM_GBPS:.1%}); kv_store bulk fill at {store_gbps / copy_gbps:.0%} of it")
     rope_info = None
     if not args.no_extras:
         # the same bulk fill through the store with rotary embedding of K, and the
@@ -373,6 +395,8 @@ def main():
         "attn_pct_of_peak": round(100 * kv_b / ((attn_us + merge_ms.mean() * 1e3) * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
         "kv_store_bulk_GBps": round(store_gbps, 1),
         "kv_store_bulk_pct_of_peak": round(100 * store_gbps / PEAK_HBM_GBPS, 2),
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "copy_ceiling_kernel": "torch copy_ of 1 GiB int64 to 1 GiB (read + write bytes counted), median of 10",
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode (split-KV attention)",
