@@ -16,7 +16,7 @@ steps read different copies of the pool ("layers"), so no step finds the
 previous step's K/V in the 256 MB Infinity Cache.  Prints ONE JSON line on
 stdout; details go to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--config 1..5] [--eager] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -65,7 +65,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=25)
-    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--workload", default="llama3_8b_decode",
+                    help="tiny_gqa, llama3_8b_decode (default), ragged_batch, long_context or mha_page1")
     ap.add_argument("--layers", type=int, default=3, help="pool copies rotated over consecutive steps")
     ap.add_argument("--splits", type=int, default=None, help="override the split heuristic")
     ap.add_argument("--kernel", choices=["mfma", "valu"], default="mfma",
@@ -211,7 +212,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    cfg = W.CONFIGS[args.config]
+    cfg = W.WORKLOADS[args.workload]
     log(f"[bench] workload {cfg.name}: {cfg.describe()}")
     t = time.perf_counter()
     inp = W.make_inputs(cfg)

@@ -38,7 +38,7 @@ SEED_BASE = 20260000
 
 @dataclass(frozen=True)
 class Config:
-    cid: int
+    seed_id: int         # the inputs are drawn from seed SEED_BASE + seed_id
     name: str
     B: int
     Hq: int
@@ -78,24 +78,24 @@ class Config:
                 f"pool={self.num_pages} pages seq_len={lens} q_std={self.q_std}")
 
 
-CONFIGS = {
-    1: Config(1, "tiny_gqa", B=2, Hq=4, Hkv=1, D=64, P=16, num_pages=32, seq_len=None,
-              seq_lens=(37, 100)),
-    2: Config(2, "llama3_8b_decode", B=32, Hq=32, Hkv=8, D=128, P=16, num_pages=9000,
-              seq_len=4096),
-    3: Config(3, "ragged_batch", B=64, Hq=32, Hkv=8, D=128, P=16, num_pages=32768,
-              seq_len=None, ragged_max=8192),
-    4: Config(4, "long_context", B=4, Hq=64, Hkv=8, D=128, P=16, num_pages=18432,
-              seq_len=65536, q_std=1.5),
-    5: Config(5, "mha_page1", B=128, Hq=16, Hkv=16, D=64, P=1, num_pages=300000,
-              seq_len=2048),
+WORKLOADS = {
+    "tiny_gqa": Config(1, "tiny_gqa", B=2, Hq=4, Hkv=1, D=64, P=16, num_pages=32,
+                       seq_len=None, seq_lens=(37, 100)),
+    "llama3_8b_decode": Config(2, "llama3_8b_decode", B=32, Hq=32, Hkv=8, D=128, P=16,
+                               num_pages=9000, seq_len=4096),
+    "ragged_batch": Config(3, "ragged_batch", B=64, Hq=32, Hkv=8, D=128, P=16,
+                           num_pages=32768, seq_len=None, ragged_max=8192),
+    "long_context": Config(4, "long_context", B=4, Hq=64, Hkv=8, D=128, P=16,
+                           num_pages=18432, seq_len=65536, q_std=1.5),
+    "mha_page1": Config(5, "mha_page1", B=128, Hq=16, Hkv=16, D=64, P=1, num_pages=300000,
+                        seq_len=2048),
 }
 
 
-def custom_config(cid=0, name="custom", **kw) -> Config:
+def custom_config(seed_id=0, name="custom", **kw) -> Config:
     """A workload of any shape (parity edge cases)."""
     kw.setdefault("seq_len", None)
-    return Config(cid, name, **kw)
+    return Config(seed_id, name, **kw)
 
 
 @dataclass
@@ -170,7 +170,7 @@ def draw_seq_lens(cfg: Config, rng) -> np.ndarray:
 
 def make_inputs(cfg: Config, seed: int | None = None, seq_lens=None) -> Inputs:
     """Draw one decode step's inputs for ``cfg`` (see the module docstring)."""
-    seed = SEED_BASE + cfg.cid if seed is None else seed
+    seed = SEED_BASE + cfg.seed_id if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     q_ss, k_ss, v_ss = np.random.SeedSequence(seed).spawn(3)
     lens = draw_seq_lens(cfg, rng) if seq_lens is None else np.asarray(seq_lens, np.int32)
@@ -243,7 +243,7 @@ def bulk_fill_rows(inp: Inputs, seed: int | None = None):
     (positions in order), the workload on which kv_store bandwidth is measured.
     Returns (k_rows uint16 [n, Hkv*D], v_rows, slots int32 [n])."""
     cfg = inp.cfg
-    ss = np.random.SeedSequence((SEED_BASE + 1000 + cfg.cid) if seed is None else seed)
+    ss = np.random.SeedSequence((SEED_BASE + 1000 + cfg.seed_id) if seed is None else seed)
     k_ss, v_ss = ss.spawn(2)
     slots = []
     for b in range(cfg.B):
@@ -260,7 +260,7 @@ def bulk_fill_rows(inp: Inputs, seed: int | None = None):
 class PrefillConfig:
     """A paged prefill batch: request b has kv_lens[b] tokens in the pool, the
     last q_lens[b] of which are its new query rows (packed over the batch)."""
-    cid: int
+    seed_id: int
     name: str
     Hq: int
     Hkv: int
@@ -297,8 +297,8 @@ def make_prefill_inputs(cfg: PrefillConfig, seed: int | None = None):
     page_table int32 [B, max_pages], kv_lens int32 [B], qo_indptr int32 [B+1]).
     The pools and page table are drawn as for a decode step over kv_lens (all
     positions stored, unowned pages NaN canaries); q ~ N(0, 1) rounded to bf16."""
-    seed = SEED_BASE + cfg.cid if seed is None else seed
-    dcfg = Config(cfg.cid, cfg.name, B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, P=cfg.P,
+    seed = SEED_BASE + cfg.seed_id if seed is None else seed
+    dcfg = Config(cfg.seed_id, cfg.name, B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, P=cfg.P,
                   num_pages=cfg.num_pages, seq_len=None, seq_lens=tuple(cfg.kv_lens))
     inp = make_inputs(dcfg, seed=seed)
     k_pool, v_pool = inp.pools_after_store()
@@ -411,7 +411,7 @@ def sample_rows(cfg: Config, k: int, seed: int = 7) -> np.ndarray:
     return np.stack([idx // cfg.Hq, idx % cfg.Hq], axis=1)
 
 
-__all__ = ["Config", "CONFIGS", "Inputs", "make_inputs", "custom_config", "contiguous_layout",
+__all__ = ["Config", "WORKLOADS", "Inputs", "make_inputs", "custom_config", "contiguous_layout",
            "bulk_fill_rows", "kv_bytes", "attention_bytes", "store_bytes", "roofline_us",
            "to_bf16_bits", "bf16_bits_to_f32", "sample_rows", "IndexingConfig", "INDEXING",
            "make_indexing_inputs", "indexing_bytes", "rope_tables", "PrefillConfig", "PREFILL",

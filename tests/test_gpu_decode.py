@@ -25,11 +25,11 @@ def decode_kernel(request, monkeypatch):
     return request.param
 
 
-def inputs(cid):
-    if cid not in _cache:
+def inputs(wl):
+    if wl not in _cache:
         _cache.clear()
-        _cache[cid] = W.make_inputs(W.CONFIGS[cid])
-    return _cache[cid]
+        _cache[wl] = W.make_inputs(W.WORKLOADS[wl])
+    return _cache[wl]
 
 
 def _oracle_full(inp):
@@ -37,17 +37,17 @@ def _oracle_full(inp):
     return oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_decode_step_matches_oracle(gpu_device, cid):
-    inp = inputs(cid)
+@pytest.mark.parametrize("wl", ["tiny_gqa", "llama3_8b_decode", "ragged_batch", "long_context", "mha_page1"])
+def test_decode_step_matches_oracle(gpu_device, wl):
+    inp = inputs(wl)
     S = pkv.num_splits(inp.cfg.B, inp.cfg.Hq, inp.cfg.Hkv, inp.max_seq_len, inp.cfg.P,
                        int(inp.seq_lens.sum()))
-    print(f"decode step cfg {cid} ({inp.cfg.describe()}), num_splits {S}", flush=True)
+    print(f"decode step {wl} ({inp.cfg.describe()}), num_splits {S}", flush=True)
     st = DeviceStep(inp, gpu_device)
     (out, lse), o_p, l_p = st.step(want_lse=True)
     torch.cuda.synchronize()
     ref, ref_lse = _oracle_full(inp)
-    check_attention(out, ref, f"cfg {cid}")
+    check_attention(out, ref, f"cfg {wl}")
     g_lse = lse.cpu().numpy().astype(np.float64)
     assert np.abs(g_lse - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max())
     # every partial written and finite or an exact empty split
@@ -57,13 +57,13 @@ def test_decode_step_matches_oracle(gpu_device, cid):
     assert (op[np.isneginf(lp)] == 0).all()
 
 
-@pytest.mark.parametrize("cid", [1, 2, 4])
-def test_partials_match_oracle_split_mode(gpu_device, cid):
-    inp = inputs(cid)
+@pytest.mark.parametrize("wl", ["tiny_gqa", "llama3_8b_decode", "long_context"])
+def test_partials_match_oracle_split_mode(gpu_device, wl):
+    inp = inputs(wl)
     cfg = inp.cfg
     S = pkv.num_splits(cfg.B, cfg.Hq, cfg.Hkv, inp.max_seq_len, cfg.P, int(inp.seq_lens.sum()))
-    if cid in (1, 2):
-        S = 3 if cid == 1 else 2  # force several splits where the heuristic picks one
+    if wl in ("tiny_gqa", "llama3_8b_decode"):
+        S = 3 if wl == "tiny_gqa" else 2  # force several splits where the heuristic picks one
     st = DeviceStep(inp, gpu_device)
     st.store()
     _, o_p, l_p = st.attend(splits=S)
@@ -84,7 +84,7 @@ def test_partials_match_oracle_split_mode(gpu_device, cid):
 
 def test_merge_alone_on_oracle_partials(gpu_device):
     """decode_merge fed the oracle's partials (rounded to fp32) vs the fp64 merge."""
-    inp = inputs(1)
+    inp = inputs("tiny_gqa")
     kf, vf = inp.pools_after_store()
     S = 5
     chunk = oracle.split_chunk(inp.max_seq_len, S, inp.cfg.P)
@@ -136,9 +136,9 @@ def test_identical_keys_give_mean_of_values(gpu_device):
             assert np.abs(g[b, h] - mean[h // 4]).max() <= 2.0 ** -8 * np.abs(mean[h // 4]).max() + 1e-3
 
 
-@pytest.mark.parametrize("cid", [1, 3])
-def test_paged_equals_contiguous_bitwise(gpu_device, cid):
-    inp = inputs(cid)
+@pytest.mark.parametrize("wl", ["tiny_gqa", "ragged_batch"])
+def test_paged_equals_contiguous_bitwise(gpu_device, wl):
+    inp = inputs(wl)
     st = DeviceStep(inp, gpu_device)
     out1, _, _ = st.step()
     kc, vc, ptc = W.contiguous_layout(inp)
@@ -149,7 +149,7 @@ def test_paged_equals_contiguous_bitwise(gpu_device, cid):
 
 
 def test_run_to_run_determinism(gpu_device):
-    inp = inputs(2)
+    inp = inputs("llama3_8b_decode")
     st = DeviceStep(inp, gpu_device)
     st.store()
     a, _, _ = st.attend()
@@ -160,7 +160,7 @@ def test_run_to_run_determinism(gpu_device):
 
 def test_split_count_invariance(gpu_device):
     """S = 1 and S = k agree to within one bf16 rounding step."""
-    inp = inputs(2)
+    inp = inputs("llama3_8b_decode")
     st = DeviceStep(inp, gpu_device)
     st.store()
     outs = [host_f64_from_bf16(st.attend(splits=s)[0]) for s in (1, 2, 5, 16)]
@@ -169,7 +169,7 @@ def test_split_count_invariance(gpu_device):
 
 
 def test_value_scaling_by_power_of_two_is_exact(gpu_device):
-    inp = inputs(1)
+    inp = inputs("tiny_gqa")
     st = DeviceStep(inp, gpu_device)
     out1, _, _ = st.step(splits=2)
     st.v_pool.mul_(2.0 ** 5)
@@ -209,7 +209,7 @@ def test_empty_sequence_and_empty_splits(gpu_device):
 
 
 def test_canary_reaches_output_when_store_is_skipped(gpu_device):
-    inp = inputs(1)
+    inp = inputs("tiny_gqa")
     st = DeviceStep(inp, gpu_device)
     out, _, _ = st.attend()
     torch.cuda.synchronize()
@@ -217,7 +217,7 @@ def test_canary_reaches_output_when_store_is_skipped(gpu_device):
 
 
 def test_bad_page_id_poisons_only_its_row(gpu_device):
-    inp = inputs(1)
+    inp = inputs("tiny_gqa")
     pt = inp.page_table.copy()
     pt[1, 2] = inp.cfg.num_pages + 5
     st = DeviceStep(inp, gpu_device, page_table=pt)
@@ -238,7 +238,7 @@ def test_max_splits(gpu_device):
 
 
 def test_errors_raise(gpu_device):
-    inp = inputs(1)
+    inp = inputs("tiny_gqa")
     st = DeviceStep(inp, gpu_device)
     with pytest.raises(RuntimeError):
         pkv.paged_decode_attn(st.q.float(), st.k_pool, st.v_pool, st.page_table, st.seq_lens, 100)
@@ -251,7 +251,7 @@ def test_errors_raise(gpu_device):
 
 def test_nan_query_gives_nan_rows(gpu_device):
     """Every score of a row NaN: the row is NaN (as in the oracle), not an empty split's zeros."""
-    inp = inputs(1)
+    inp = inputs("tiny_gqa")
     q = inp.q.copy()
     q[1, 2] = W.BF16_NAN
     st = DeviceStep(inp, gpu_device)

@@ -44,16 +44,16 @@ def run_both(inp, dev, splits, max_len=None, slots=None, new_rows=None, outputs=
     return got
 
 
-@pytest.mark.parametrize("cid,splits", [(1, 1), (2, 1), (2, 3), (3, None), (4, None), (5, 1)])
-def test_fused_step_equals_store_then_attention(gpu_device, cid, splits):
-    inp = W.make_inputs(W.CONFIGS[cid])
+@pytest.mark.parametrize("wl,splits", [("tiny_gqa", 1), ("llama3_8b_decode", 1), ("llama3_8b_decode", 3), ("ragged_batch", None), ("long_context", None), ("mha_page1", 1)])
+def test_fused_step_equals_store_then_attention(gpu_device, wl, splits):
+    inp = W.make_inputs(W.WORKLOADS[wl])
     S = splits or pkv.num_splits(inp.cfg.B, inp.cfg.Hq, inp.cfg.Hkv, inp.max_seq_len, inp.cfg.P,
                                  int(inp.seq_lens.sum()))
-    print(f"fused step cfg {cid} ({inp.cfg.describe()}), num_splits {S}", flush=True)
+    print(f"fused step {wl} ({inp.cfg.describe()}), num_splits {S}", flush=True)
     out, _ = run_both(inp, gpu_device, S)
     kf, vf = inp.pools_after_store()
     ref, _ = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
-    check_attention(out, ref, f"fused step cfg {cid} S={S}")
+    check_attention(out, ref, f"fused step {wl} S={S}")
 
 
 def test_fused_step_edges(gpu_device):

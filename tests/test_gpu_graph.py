@@ -36,13 +36,13 @@ def _layer_inputs(inp, n_layers, dev):
     return layers
 
 
-@pytest.mark.parametrize("cid,n_layers,splits,fused", [(1, 3, 2, True), (3, 2, None, True), (2, 2, 1, True),
-                                                      (1, 2, 2, False), (2, 2, 1, False)])
-def test_replays_equal_the_eager_step(gpu_device, cid, n_layers, splits, fused):
-    base = W.make_inputs(W.CONFIGS[cid])
+@pytest.mark.parametrize("wl,n_layers,splits,fused", [("tiny_gqa", 3, 2, True), ("ragged_batch", 2, None, True), ("llama3_8b_decode", 2, 1, True),
+                                                      ("tiny_gqa", 2, 2, False), ("llama3_8b_decode", 2, 1, False)])
+def test_replays_equal_the_eager_step(gpu_device, wl, n_layers, splits, fused):
+    base = W.make_inputs(W.WORKLOADS[wl])
     layers = _layer_inputs(base, n_layers, gpu_device)
     total = int(base.seq_lens.sum())
-    print(f"graph step cfg {cid}, {n_layers} layers, splits {splits}, fused {fused}", flush=True)
+    print(f"graph step {wl}, {n_layers} layers, splits {splits}, fused {fused}", flush=True)
     # graph side: one set of device tensors per layer (page table, lengths, slots shared)
     dsteps = [DeviceStep(li, gpu_device) for li in layers]
     shared = dsteps[0]
@@ -66,12 +66,12 @@ def test_replays_equal_the_eager_step(gpu_device, cid, n_layers, splits, fused):
     # and the replayed result is the oracle's
     kf, vf = layers[-1].pools_after_store()
     ref, _ = oracle.paged_decode(layers[-1].q, kf, vf, layers[-1].page_table, layers[-1].seq_lens)
-    check_attention(g.outputs[-1], ref, f"graph cfg {cid}")
+    check_attention(g.outputs[-1], ref, f"graph {wl}")
 
 
 def test_replay_follows_inputs_refilled_in_place(gpu_device):
     """Static buffers: new q written in place between replays is what the next replay reads."""
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     d = DeviceStep(inp, gpu_device)
     g = StepGraph([(d.k_pool, d.v_pool)], d.q, d.k_new, d.v_new, d.page_table, d.seq_lens,
                   d.slot_mapping, inp.max_seq_len, 2)

@@ -33,19 +33,19 @@ def same_bits(a, b):
                        b.contiguous().view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32))
 
 
-@pytest.mark.parametrize("cid,splits", [(1, 1), (2, 1), (2, 2), (3, None), (5, 1)])
-def test_merged_equals_attention_then_merge(gpu_device, cid, splits):
-    inp = W.make_inputs(W.CONFIGS[cid])
+@pytest.mark.parametrize("wl,splits", [("tiny_gqa", 1), ("llama3_8b_decode", 1), ("llama3_8b_decode", 2), ("ragged_batch", None), ("mha_page1", 1)])
+def test_merged_equals_attention_then_merge(gpu_device, wl, splits):
+    inp = W.make_inputs(W.WORKLOADS[wl])
     S = splits or pkv.num_splits(inp.cfg.B, inp.cfg.Hq, inp.cfg.Hkv, inp.max_seq_len, inp.cfg.P,
                                  int(inp.seq_lens.sum()))
-    print(f"merged decode cfg {cid} ({inp.cfg.describe()}), num_splits {S}", flush=True)
+    print(f"merged decode {wl} ({inp.cfg.describe()}), num_splits {S}", flush=True)
     st = DeviceStep(inp, gpu_device)
     st.store()
     out, lse, ref_out, ref_lse = both(st, S)
     assert same_bits(out, ref_out) and same_bits(lse, ref_lse)
     kf, vf = inp.pools_after_store()
     ref, _ = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
-    check_attention(out, ref, f"merged cfg {cid} S={S}")
+    check_attention(out, ref, f"merged {wl} S={S}")
 
 
 def test_merged_degenerate_rows(gpu_device):
@@ -65,7 +65,7 @@ def test_merged_degenerate_rows(gpu_device):
 
 
 def test_merged_one_split_needs_no_partials(gpu_device):
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     st = DeviceStep(inp, gpu_device)
     st.store()
     out = pkv.paged_decode_attn_merged(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens,

@@ -34,11 +34,11 @@ def rotated_step(inp):
     return pos, qpos, kf.reshape(inp.k_pool.shape), vf.reshape(inp.v_pool.shape), q_rot
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_store_rope_pools_bit_exact(gpu_device, cid):
-    inp = W.make_inputs(W.CONFIGS[cid])
+@pytest.mark.parametrize("wl", ["tiny_gqa", "llama3_8b_decode", "ragged_batch", "long_context", "mha_page1"])
+def test_store_rope_pools_bit_exact(gpu_device, wl):
+    inp = W.make_inputs(W.WORKLOADS[wl])
     cfg = inp.cfg
-    print(f"store+rope cfg {cid}: {cfg.describe()}", flush=True)
+    print(f"store+rope {wl}: {cfg.describe()}", flush=True)
     pos, _, kf, vf, _ = rotated_step(inp)
     _, _, cd, sd = tables(gpu_device, max(int(inp.seq_lens.max()), 1), cfg.D)
     st = DeviceStep(inp, gpu_device)
@@ -68,9 +68,9 @@ def test_store_rope_bulk_fill_bit_exact(gpu_device, D, Hkv):
     assert host_u16(kp).tobytes() == kf.tobytes() and host_u16(vp).tobytes() == vf.tobytes()
 
 
-@pytest.mark.parametrize("cid,splits", [(1, 3), (2, None), (4, None), (5, None)])
-def test_attention_rope_equals_attention_on_rotated_q(gpu_device, cid, splits):
-    inp = W.make_inputs(W.CONFIGS[cid])
+@pytest.mark.parametrize("wl,splits", [("tiny_gqa", 3), ("llama3_8b_decode", None), ("long_context", None), ("mha_page1", None)])
+def test_attention_rope_equals_attention_on_rotated_q(gpu_device, wl, splits):
+    inp = W.make_inputs(W.WORKLOADS[wl])
     cfg = inp.cfg
     pos, qpos, kf, vf, q_rot = rotated_step(inp)
     _, _, cd, sd = tables(gpu_device, max(int(inp.seq_lens.max()), 1), cfg.D)
@@ -87,11 +87,11 @@ def test_attention_rope_equals_attention_on_rotated_q(gpu_device, cid, splits):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     ref, _ = oracle.paged_decode(q_rot, kf, vf, inp.page_table, inp.seq_lens)
-    check_attention(out1, ref, f"rope attention cfg {cid}")
+    check_attention(out1, ref, f"rope attention {wl}")
 
 
 def test_positions_outside_the_table_give_nan_rows(gpu_device):
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     cfg = inp.cfg
     _, _, cd, sd = tables(gpu_device, 64, cfg.D)          # table shorter than position 99
     st = DeviceStep(inp, gpu_device)
@@ -111,7 +111,7 @@ def test_positions_outside_the_table_give_nan_rows(gpu_device):
 
 
 def test_rope_argument_errors(gpu_device):
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     cfg = inp.cfg
     st = DeviceStep(inp, gpu_device)
     _, _, cd, sd = tables(gpu_device, 128, cfg.D)

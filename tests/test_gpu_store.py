@@ -21,10 +21,10 @@ def _bytes_dev(a: np.ndarray, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_step_store_whole_pool_bit_exact(gpu_device, cid):
-    inp = W.make_inputs(W.CONFIGS[cid])
-    print(f"store step cfg {cid}: {inp.cfg.describe()}", flush=True)
+@pytest.mark.parametrize("wl", ["tiny_gqa", "llama3_8b_decode", "ragged_batch", "long_context", "mha_page1"])
+def test_step_store_whole_pool_bit_exact(gpu_device, wl):
+    inp = W.make_inputs(W.WORKLOADS[wl])
+    print(f"store step {wl}: {inp.cfg.describe()}", flush=True)
     st = DeviceStep(inp, gpu_device)
     st.store()
     torch.cuda.synchronize()
@@ -90,13 +90,13 @@ def test_store_strided_and_misaligned(gpu_device):
         assert (dk.cpu().numpy() == ek).all() and (dv.cpu().numpy() == ev).all(), off
 
 
-@pytest.mark.parametrize("cid", [1, 2, 5])
-def test_bulk_fill_bit_exact(gpu_device, cid):
+@pytest.mark.parametrize("wl", ["tiny_gqa", "llama3_8b_decode", "mha_page1"])
+def test_bulk_fill_bit_exact(gpu_device, wl):
     """Every position of every sequence stored in one call (the bandwidth workload)."""
-    inp = W.make_inputs(W.CONFIGS[cid])
+    inp = W.make_inputs(W.WORKLOADS[wl])
     cfg = inp.cfg
     k_rows, v_rows, slots = W.bulk_fill_rows(inp)
-    print(f"bulk fill cfg {cid}: {slots.shape[0]} rows", flush=True)
+    print(f"bulk fill {wl}: {slots.shape[0]} rows", flush=True)
     flat = lambda a: a.reshape(cfg.num_pages * cfg.P, cfg.row_elems)
     dk = bf16_dev(flat(inp.k_pool), gpu_device)
     dv = bf16_dev(flat(inp.v_pool), gpu_device)

@@ -27,7 +27,7 @@ def _f64(bits):
 
 def small_cases():
     """Tiny shapes spanning G in {1,2,4,8}, D in {64,128}, page sizes 1..16, ragged lengths."""
-    yield W.CONFIGS[1], None
+    yield W.WORKLOADS["tiny_gqa"], None
     yield W.custom_config(name="g8_d128_p4", B=3, Hq=16, Hkv=2, D=128, P=4, num_pages=64,
                           seq_lens=(1, 23, 50)), None
     yield W.custom_config(name="mha_p1", B=2, Hq=3, Hkv=3, D=64, P=1, num_pages=200,
@@ -86,7 +86,7 @@ def test_store_rejects_out_of_range_slot():
 
 def test_store_of_generated_step_restores_the_drawn_pool():
     """Storing the step's rows over the canaries gives back the drawn pool."""
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     cfg = inp.cfg
     flat = lambda a: a.reshape(cfg.num_pages * cfg.P, cfg.row_elems)
     ko, vo = oracle.kv_store(flat(inp.k_pool), flat(inp.v_pool), inp.k_new, inp.v_new, inp.slot_mapping)
@@ -133,7 +133,7 @@ def test_attention_matches_torch_sdpa_fp64(case):
 
 
 def test_softmax_weights_sum_to_one():
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     kf, vf = _after_store(inp)
     for b in range(2):
         for h in range(4):
@@ -191,7 +191,7 @@ def test_paged_equals_contiguous_bitwise(case):
 
 
 def test_rows_mode_equals_full_mode():
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     kf, vf = _after_store(inp)
     out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
     rows = np.array([[1, 3], [0, 0], [1, 0]])
@@ -202,7 +202,7 @@ def test_rows_mode_equals_full_mode():
 
 def test_value_scaling_by_power_of_two_is_exact():
     """Scaling V by 2^k scales the output by exactly 2^k."""
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     kf, vf = _after_store(inp)
     out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
     v32 = W.bf16_bits_to_f32(vf)
@@ -215,7 +215,7 @@ def test_value_scaling_by_power_of_two_is_exact():
 
 def test_canaries_reach_the_output_when_the_store_is_skipped():
     """Before the store, the new-token slot holds NaN: attention must see it."""
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     out, _ = oracle.paged_decode(inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens)
     assert np.isnan(out).all()
     kf, vf = _after_store(inp)
@@ -245,7 +245,7 @@ def test_split_chunk_reading():
 
 @pytest.mark.parametrize("S", [1, 2, 3, 5, 8])
 def test_split_then_merge_equals_unsplit(S):
-    inp = W.make_inputs(W.CONFIGS[1])
+    inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     kf, vf = _after_store(inp)
     out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
     chunk = oracle.split_chunk(inp.max_seq_len, S, inp.cfg.P)
