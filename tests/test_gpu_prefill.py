@@ -56,6 +56,32 @@ def test_shapes_and_ragged_tails(gpu_device, D, G, P):
         check_lse(lse, ref_lse)
 
 
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_empty_requests_in_the_batch(gpu_device, G):
+    """Requests with no query rows (q_len = 0) among others get no Q tile, and
+    the rows after them still find their own request."""
+    Hkv, D, P = 2, 128, 16
+    q_lens = (0, 37, 0, 64, 0, 1)
+    kv_lens = (10, 100, 5, 64, 33, 20)
+    cfg = W.PrefillConfig(0, f"empty_requests_g{G}", G * Hkv, Hkv, D, P,
+                          -(-sum(kv_lens) // P) + len(kv_lens) + 4, q_lens, kv_lens)
+    q, kp, vp, pt, kl, qo = W.make_prefill_inputs(cfg)
+    for causal in (True, False):
+        print(f"prefill with empty requests G={G} causal={causal}: {cfg.describe()}", flush=True)
+        out, lse = run(q, kp, vp, pt, kl, qo, gpu_device, causal)
+        ref, ref_lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, causal)
+        check_attention(out, ref, f"prefill empty requests G{G} causal={causal}")
+        check_lse(lse, ref_lse)
+
+
+def test_batch_with_no_query_rows(gpu_device):
+    """Every request empty: no tile, nothing launched, empty outputs."""
+    cfg = W.PrefillConfig(0, "no_rows", 8, 2, 128, 16, 8, (0, 0), (5, 9))
+    q, kp, vp, pt, kl, qo = W.make_prefill_inputs(cfg)
+    out, lse = run(q, kp, vp, pt, kl, qo, gpu_device)
+    assert tuple(out.shape) == (0, 8, 128) and tuple(lse.shape) == (0, 8)
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_chunked", "llama3_8b_fresh"])
 def test_full_size_on_sampled_rows(gpu_device, name):
     cfg = W.PREFILL[name]
