@@ -41,7 +41,7 @@ def test_page_example_batch(gpu_device, causal):
 
 
 @pytest.mark.parametrize("D,G,P", [(64, 1, 1), (64, 2, 16), (64, 8, 4), (128, 1, 16), (128, 4, 16),
-                                   (128, 8, 1), (128, 2, 256)])
+                                   (128, 8, 1), (128, 2, 256), (64, 4, 1024), (128, 8, 512)])
 def test_shapes_and_ragged_tails(gpu_device, D, G, P):
     Hkv = 2
     q_lens = (1, 63, 64, 65, 130, 7)
