@@ -149,6 +149,8 @@ struct TileLoader {
   static constexpr int RPI = 64 / LPR;       // rows per direct load (64 lanes)
   static constexpr int RWV = kKT / W;        // tile rows loaded by each wave
   static constexpr int NI = RWV / RPI;       // direct loads per wave, tile and tensor
+  // the fast path reads a wave's RWV rows from one page of >= 16 tokens
+  static_assert(RWV <= 16, "a wave's rows of a tile must fit in one 16-token page");
 
   const PrefillParams &p;
   const int32_t *pt;                         // the request's page-table row
