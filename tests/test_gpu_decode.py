@@ -193,6 +193,24 @@ def test_shapes_and_ragged_tails(gpu_device, D, G, P):
         check_attention(out, _oracle_full(inp)[0], f"D{D} G{G} P{P} S{S}")
 
 
+@pytest.mark.parametrize("D,G,P,lens,S", [
+    (64, 4, 1, (5000, 2100, 1), 1),       # 5000 page ids in one split: three LDS segments
+    (64, 1, 1, (4097,), 2),               # two splits of 2049 pages: each past one segment
+    (128, 4, 16, (40000, 33000), 1),      # 2500 and 2063 pages: two segments each
+])
+def test_splits_longer_than_one_page_id_segment(gpu_device, D, G, P, lens, S):
+    """A split whose pages exceed the 2048 page ids staged in LDS at a time
+    refetches them segment by segment."""
+    cfg = W.custom_config(name=f"long_split_d{D}g{G}p{P}", B=len(lens), Hq=G, Hkv=1, D=D, P=P,
+                          num_pages=-(-sum(lens) // P) + len(lens) + 3, seq_lens=lens)
+    inp = W.make_inputs(cfg)
+    print(f"long splits D{D} G{G} P{P} lens {lens} S{S}", flush=True)
+    st = DeviceStep(inp, gpu_device)
+    out, _, _ = st.step(splits=S)
+    torch.cuda.synchronize()
+    check_attention(out, _oracle_full(inp)[0], f"long splits D{D} G{G} P{P} S{S}")
+
+
 def test_empty_sequence_and_empty_splits(gpu_device):
     cfg = W.custom_config(B=3, Hq=4, Hkv=1, D=64, P=16, num_pages=20, seq_lens=(0, 3, 200))
     inp = W.make_inputs(cfg)
