@@ -74,3 +74,16 @@ def test_fused_step_edges(gpu_device):
     bad = slots.copy()
     bad[1] = cfg.num_pages * cfg.P + 3
     run_both(inp, gpu_device, 1, max_len=129, slots=bad, new_rows=(kn, vn), outputs=False)
+
+
+@pytest.mark.parametrize("D,G,P,lens,S", [(64, 4, 1, (5000, 2100, 1), 1), (128, 4, 16, (40000, 33000), 1)])
+def test_fused_step_with_splits_longer_than_one_page_id_segment(gpu_device, D, G, P, lens, S):
+    """The new token's position lies past the first LDS segment of page ids."""
+    cfg = W.custom_config(name=f"fused_long_split_d{D}p{P}", B=len(lens), Hq=G, Hkv=1, D=D, P=P,
+                          num_pages=-(-sum(lens) // P) + len(lens) + 3, seq_lens=lens)
+    inp = W.make_inputs(cfg)
+    print(f"fused step, long splits D{D} P{P} lens {lens} S{S}", flush=True)
+    out, _ = run_both(inp, gpu_device, S)
+    kf, vf = inp.pools_after_store()
+    ref, _ = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    check_attention(out, ref, f"fused step long splits D{D} P{P}")
