@@ -449,7 +449,9 @@ template <int D, int G, int kMode>
 hipError_t launch_mfma(const DecodeParams &p, hipStream_t stream) {
   constexpr int kWaves = 4;
   const dim3 grid{unsigned(p.num_splits * p.Hkv * p.B)}, block{kWaves * 64};
-  constexpr int NBUF = D == 128 ? 3 : 4;
+  // tiles in the register ring: with 8 heads at D = 128 a ring of two keeps
+  // the kernel within 256 registers, so two workgroups share a CU
+  constexpr int NBUF = D == 128 ? (G == 8 ? 2 : 3) : 4;
   if (p.page_log2 >= 4)
     hipLaunchKernelGGL((paged_decode_mfma_kernel<D, G, true, NBUF, kWaves, kMode>), grid, block, 0,
                        stream, p);
