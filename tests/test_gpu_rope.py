@@ -68,7 +68,9 @@ def test_store_rope_bulk_fill_bit_exact(gpu_device, D, Hkv):
     assert host_u16(kp).tobytes() == kf.tobytes() and host_u16(vp).tobytes() == vf.tobytes()
 
 
-@pytest.mark.parametrize("wl,splits", [("tiny_gqa", 3), ("llama3_8b_decode", None), ("long_context", None), ("mha_page1", None)])
+# long_context at one split: 4096 page ids per split, refetched from LDS in two segments
+@pytest.mark.parametrize("wl,splits", [("tiny_gqa", 3), ("llama3_8b_decode", None), ("long_context", None),
+                                       ("long_context", 1), ("mha_page1", None)])
 def test_attention_rope_equals_attention_on_rotated_q(gpu_device, wl, splits):
     inp = W.make_inputs(W.WORKLOADS[wl])
     cfg = inp.cfg
