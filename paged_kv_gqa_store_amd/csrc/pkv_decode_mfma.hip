@@ -113,10 +113,40 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // one-dimensional grid: kv head fastest, then sequence, then split
-  const int g = blockIdx.x % p.Hkv;
-  const int b = (blockIdx.x / p.Hkv) % p.B;
-  const int s = blockIdx.x / (p.Hkv * p.B);
+  // one-dimensional grid: kv head fastest, then the (sequence, split) pairs,
+  // sequence before split; with few pairs and several splits (a ragged batch)
+  // the pairs go longest first instead.  Either order is a function of the
+  // arguments only, and a pair's result does not depend on its workgroup.
+  int g = blockIdx.x % p.Hkv, b, s;
+  if (p.longest_first) {
+    __shared__ int sm_len[kWaves * 64];
+    __shared__ int sm_pick;
+    const int n = p.B * p.num_splits;   // <= kWaves * 64 (checked on the host)
+    const int i = threadIdx.x;
+    if (i < n) {
+      const int Li = min(max(p.seq_lens[i % p.B], 0), p.max_pages << p.page_log2);
+      sm_len[i] = max(0, min(p.chunk, Li - (i / p.B) * p.chunk));
+    }
+    __syncthreads();
+    // rank = pairs longer than this one, or as long with a lower index: a
+    // permutation of 0 .. n-1, so exactly one thread matches
+    const int target = blockIdx.x / p.Hkv;
+    if (i < n) {
+      const int li = sm_len[i];
+      int r = 0;
+      for (int j = 0; j < n; ++j) {
+        const int lj = sm_len[j];
+        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
+      }
+      if (r == target) sm_pick = i;
+    }
+    __syncthreads();
+    b = sm_pick % p.B;
+    s = sm_pick / p.B;
+  } else {
+    b = (blockIdx.x / p.Hkv) % p.B;
+    s = blockIdx.x / (p.Hkv * p.B);
+  }
   const int log2P = p.page_log2;
   const int pmask = (1 << log2P) - 1;
   const int32_t *pt = p.page_table + size_t(b) * p.max_pages;

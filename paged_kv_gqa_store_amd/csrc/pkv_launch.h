@@ -20,6 +20,7 @@ struct DecodeParams {
   int page_log2;             // page_size = 1 << page_log2
   int num_pages, max_pages;
   int num_splits, chunk;     // split s covers [s*chunk, (s+1)*chunk)
+  int longest_first;         // workgroups take the (sequence, split) pairs longest first
   float scale_log2;          // softmax scale * log2(e)
   // rotary embedding of q (all NULL / 0 when q is used as given)
   const int32_t *q_pos;      // [B] position of each sequence's query token
