@@ -21,7 +21,8 @@
 //   Page ids of a split are staged in LDS (fetched together with the
 //   sequence length); each wave streams a contiguous range of tiles through
 //   a ring of register buffers, with two (D=128) or three (D=64) tiles in
-//   flight while one is computed.
+//   flight while one is computed (one with 8 q heads at D=128, which keeps
+//   the kernel within 256 registers: two workgroups per CU).
 //   K and V are read once, so their loads carry the non-temporal hint: on
 //   gfx950 this measured ~10% faster than default-policy loads of the same
 //   addresses (the lines are not kept in L2 / the memory-side cache).
@@ -29,6 +30,8 @@
 //   split this keeps the kv heads of a sequence (which read the same pages)
 //   launched together; with several, every sequence's first split is
 //   dispatched before any second split, so long ragged sequences start early.
+//   With several splits and at most 256 (sequence, split) pairs, the pairs
+//   go longest first (ranked in LDS by every workgroup).
 #include <math.h>
 
 #include "pkv_device.h"
