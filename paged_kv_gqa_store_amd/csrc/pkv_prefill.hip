@@ -474,19 +474,25 @@ __global__ __launch_bounds__(W * 64) void paged_prefill32_kernel(PrefillParams p
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
-    // (the next k-step's K fragments are read while this one's products run)
-    u32x4 ka[2][2];
+    // (the K fragments of k-step j + RA are read while step j's products run;
+    // the scheduling barrier keeps the compiler from sinking those reads back
+    // next to their use)
+    constexpr int RA = 3;
+    u32x4 ka[RA + 1][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) ka[0][mb] = *reinterpret_cast<const u32x4 *>(kb + koff[0] + 32 * mb * PITCH);
+    for (int j = 0; j < RA; ++j)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) ka[j][mb] = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 32 * mb * PITCH);
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      if (j + 1 < KS)
+      if (j + RA < KS)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          ka[(j + 1) & 1][mb] = *reinterpret_cast<const u32x4 *>(kb + koff[j + 1] + 32 * mb * PITCH);
+          ka[(j + RA) % (RA + 1)][mb] = *reinterpret_cast<const u32x4 *>(kb + koff[j + RA] + 32 * mb * PITCH);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[j & 1][mb]), qb[j], s[mb], 0, 0, 0);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[j % (RA + 1)][mb]), qb[j], s[mb], 0, 0, 0);
     }
     float tmax = -INFINITY;
     if (!full_tile) {
