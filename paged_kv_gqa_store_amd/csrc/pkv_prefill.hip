@@ -313,14 +313,22 @@ __global__ __launch_bounds__(kThreads) void paged_prefill16_kernel(PrefillParams
     const bool full_tile = t0 + kKT <= kv_end && (!p.causal || t0 + kKT - 1 <= w.pos_base + w.wg_row0);
     // S^T for 4 blocks of 16 tokens: lane holds tokens 16mb + 4(lane >> 4) + r
     f32x4 s[4];
+    // the next block's K fragments are read before this block's products
+    // (pinned by a scheduling barrier)
+    u32x4 ka[2][KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) ka[0][j] = *reinterpret_cast<const u32x4 *>(kb + koff[j]);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
+      if (mb + 1 < 4)
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+          ka[(mb + 1) & 1][j] = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 16 * (mb + 1) * PITCH);
+      __builtin_amdgcn_sched_barrier(0);
       s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const u32x4 ka = *reinterpret_cast<const u32x4 *>(kb + koff[j] + 16 * mb * PITCH);
-        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), qb[j], s[mb], 0, 0, 0);
-      }
+      for (int j = 0; j < KS; ++j)
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[mb & 1][j]), qb[j], s[mb], 0, 0, 0);
     }
     // mask, then the tile max of this lane's row on the raw scores (scale > 0)
     float tmax = -INFINITY;
