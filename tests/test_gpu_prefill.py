@@ -56,6 +56,27 @@ def test_shapes_and_ragged_tails(gpu_device, D, G, P):
         check_lse(lse, ref_lse)
 
 
+@pytest.mark.parametrize("D,P", [(128, 16), (128, 1), (64, 16), (64, 4)])
+def test_one_head_per_kv_head_on_tile_pairs(gpu_device, D, P):
+    """G = 1 with long requests (at least 8 host tiles of 64 rows per request
+    on average) runs 128-row workgroups over pairs of host tiles.  The tile
+    counts 21, 11, 2, 15 and 1 put request boundaries inside pairs (each side
+    then runs as a job of its own) and leave a last tile alone."""
+    Hkv = 3
+    q_lens = (1300, 700, 65, 960, 1)
+    kv_lens = (1300, 1500, 65, 2000, 9)
+    assert sum(-(-q // 64) for q in q_lens) >= 8 * len(q_lens)
+    cfg = W.PrefillConfig(0, f"pairs_d{D}_p{P}", Hkv, Hkv, D, P,
+                          -(-sum(kv_lens) // P) + len(kv_lens) + 4, q_lens, kv_lens)
+    q, kp, vp, pt, kl, qo = W.make_prefill_inputs(cfg)
+    for causal in (True, False):
+        print(f"prefill G=1 tile pairs D={D} P={P} causal={causal}: {cfg.describe()}", flush=True)
+        out, lse = run(q, kp, vp, pt, kl, qo, gpu_device, causal)
+        ref, ref_lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, causal)
+        check_attention(out, ref, f"prefill G1 pairs D{D} P{P} causal={causal}")
+        check_lse(lse, ref_lse)
+
+
 @pytest.mark.parametrize("G", [1, 2, 4])
 def test_empty_requests_in_the_batch(gpu_device, G):
     """Requests with no query rows (q_len = 0) among others get no Q tile, and
