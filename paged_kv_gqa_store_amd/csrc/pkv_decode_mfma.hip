@@ -121,6 +121,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   // the pairs go longest first instead.  Either order is a function of the
   // arguments only, and a pair's result does not depend on its workgroup.
   int g = blockIdx.x % p.Hkv, b, s;
+  bool empty_pair = false;        // a split past its sequence's end (known in the longest-first order)
   if (p.longest_first) {
     __shared__ int sm_len[kWaves * 64];
     __shared__ int sm_pick;
@@ -146,9 +147,27 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
     __syncthreads();
     b = sm_pick % p.B;
     s = sm_pick / p.B;
+    empty_pair = sm_len[sm_pick] == 0;
   } else {
     b = (blockIdx.x / p.Hkv) % p.B;
     s = blockIdx.x / (p.Hkv * p.B);
+  }
+  if (!kFuse && empty_pair) {
+    // the result of an empty split (as in the epilogue), without its loads:
+    // in a ragged batch these pairs are many, and they run last
+    for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
+      const int h = idx / D, d = idx % D;
+      const size_t frow = size_t(b) * p.Hq + size_t(g) * G + h;
+      if (p.out) {
+        p.out[frow * D + d] = 0;
+        if (d == 0 && p.lse_out) p.lse_out[frow] = -INFINITY;
+      } else {
+        const size_t orow = frow * p.num_splits + s;
+        p.o_partial[orow * D + d] = 0.f;
+        if (d == 0) p.lse_partial[orow] = -INFINITY;
+      }
+    }
+    return;
   }
   const int log2P = p.page_log2;
   const int pmask = (1 << log2P) - 1;
