@@ -39,8 +39,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, published
 # sources when the counters were taken: any edit to them voids the figure.
 COUNTED_TRAFFIC = {
     "workload": "llama3_8b_decode",
-    "sources_sha256": "49557bb3f6ab987a018cec98fcebad32e0c0fa79399fed72a12eba52539fc2a1",
-    "read_bytes": 537615170,    # FETCH_SIZE 262516.9 KiB x (1 GiB / 524307.0 KiB)
+    "sources_sha256": "3dbaaa07e16ffd896ca51ed4f180da3e95cbcfd920c90a51b25c8283d4c5d00f",
+    "read_bytes": 537616869,    # FETCH_SIZE 262517.8 KiB x (1 GiB / 524307.1 KiB)
     "write_bytes": 532480,      # WRITE_SIZE 520.0 KiB x (1 GiB / 1048576.0 KiB)
 }
 KERNEL_SOURCES = ["pkv_decode_mfma.hip", "pkv_device.h", "pkv_launch.h"]
