@@ -24,8 +24,10 @@
 // twice the rate of the 16x16x32 form in a microbenchmark on this chip
 // (independent accumulation chains); with four or more q heads per kv head
 // the workgroup has 8 waves (4 heads x 64 rows), so one K/V tile in LDS
-// serves twice the rows.  With one q head per kv head a workgroup's 64 rows
-// are spread over its 4 waves, 16 each, on the 16x16x32 form.
+// serves twice the rows.  With one q head per kv head and long requests a
+// workgroup takes a pair of host tiles, 128 rows of one head on 4 waves of
+// the 32x32 form; with short requests its 64 rows are spread over its 4
+// waves, 16 each, on the 16x16x32 form.
 // K and V tiles of 64 tokens move from the pool into LDS with direct loads
 // (global_load_lds_dwordx4: 16 bytes per lane, no registers, no staging
 // code), double-buffered, so one barrier per tile separates the loads of tile
@@ -431,12 +433,16 @@ __global__ __launch_bounds__(kThreads) void paged_prefill16_kernel(PrefillParams
     p.lse[size_t(w.q0 + my_row) * p.Hq + h] = (m + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
-// Two or more q heads per kv head: a wave owns 32 query rows of one head, on
-// the 32x32x16 form (lane & 31 = query row; register r of a 32-token block is
-// token 8(r / 4) + 4(lane >> 5) + r % 4).  HB heads per workgroup, W / HB
-// waves per head (W = 8 when HB = 4 and D = 128, else 4).
+// A wave owns 32 query rows of one head, on the 32x32x16 form (lane & 31 =
+// query row; register r of a 32-token block is token 8(r / 4) + 4(lane >> 5)
+// + r % 4).  HB heads per workgroup, W / HB waves per head (W = 8 when HB = 4
+// and D = 128, else 4), so RW = 32 W / HB rows per head: 32 or 64 rows of one
+// host tile, or with HB = 1 the 128 rows of a pair of host tiles.  The job
+// loop of the pair form would take the kernel past 256 registers (one wave
+// per SIMD); two waves per SIMD are asked for explicitly.
 template <int D, int HB, int W>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill32_kernel(PrefillParams p) {
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill32_kernel(
+    PrefillParams p) {
   constexpr int KS = D / 16;                 // k-steps of S^T over the head dimension
   constexpr int MB = D / 32;                 // 32-dim blocks of O^T
   constexpr int WPH = W / HB;                // waves per q head
