@@ -161,7 +161,7 @@ def measure_extras(args, pkv, W, dev, to_bf16, to_i32) -> dict:
     """Secondary rows of the path, each on its own synthetic workload."""
     import torch
     extras = {}
-    for name in ("llama3_8b_chunked", "llama3_8b_fresh"):
+    for name in ("llama3_8b_chunked", "llama3_8b_fresh", "mha_fresh"):
         pcfg = W.PREFILL[name]
         q, kp, vp, pt, kl, qo = W.make_prefill_inputs(pcfg)
         plan = pkv.prefill_plan(np.diff(qo), dev)

@@ -289,6 +289,9 @@ PREFILL = {
     # fresh prompts, q = kv = 2048 (the size of the page's single-batch prefill figure), batch 2
     "llama3_8b_fresh": PrefillConfig(103, "llama3_8b_fresh", 32, 8, 128, 16, 300,
                                      (2048,) * 2, (2048,) * 2),
+    # the same fresh prompts with one q head per kv head (32 + 32 heads)
+    "mha_fresh": PrefillConfig(104, "mha_fresh", 32, 32, 128, 16, 300,
+                               (2048,) * 2, (2048,) * 2),
 }
 
 

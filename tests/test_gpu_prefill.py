@@ -103,7 +103,7 @@ def test_batch_with_no_query_rows(gpu_device):
     assert tuple(out.shape) == (0, 8, 128) and tuple(lse.shape) == (0, 8)
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_chunked", "llama3_8b_fresh"])
+@pytest.mark.parametrize("name", ["llama3_8b_chunked", "llama3_8b_fresh", "mha_fresh"])
 def test_full_size_on_sampled_rows(gpu_device, name):
     cfg = W.PREFILL[name]
     print(f"prefill {name}: {cfg.describe()}", flush=True)
