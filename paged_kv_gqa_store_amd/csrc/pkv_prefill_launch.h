@@ -23,6 +23,7 @@ struct PrefillParams {
   int page_log2, num_pages, max_pages;
   int causal;
   float scale_log2;              // softmax scale * log2(e)
+  int interleave;                // set by the launcher: groups of one XCD interleave their q chunks
 };
 
 hipError_t launch_paged_prefill(const PrefillParams &p, hipStream_t stream);

@@ -77,6 +77,23 @@ def test_one_head_per_kv_head_on_tile_pairs(gpu_device, D, P):
         check_lse(lse, ref_lse)
 
 
+@pytest.mark.parametrize("D,G,Hkv", [(128, 1, 16), (64, 2, 16), (128, 4, 16)])
+def test_xcd_interleaved_work_order(gpu_device, D, G, Hkv):
+    """With at least 8 host tiles per request on average and a multiple of 8
+    kv-head groups, the groups of one XCD interleave their q chunks in the
+    work order; every row must still be computed once and right."""
+    q_lens, kv_lens = (700, 600), (900, 600)
+    assert sum(-(-q // 64) for q in q_lens) >= 8 * len(q_lens)
+    cfg = W.PrefillConfig(0, f"interleave_d{D}_g{G}_h{Hkv}", G * Hkv, Hkv, D, 16,
+                          -(-sum(kv_lens) // 16) + len(kv_lens) + 4, q_lens, kv_lens)
+    q, kp, vp, pt, kl, qo = W.make_prefill_inputs(cfg)
+    print(f"prefill interleaved order D={D} G={G} Hkv={Hkv}: {cfg.describe()}", flush=True)
+    out, lse = run(q, kp, vp, pt, kl, qo, gpu_device, True)
+    ref, ref_lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, True)
+    check_attention(out, ref, f"prefill interleaved D{D} G{G} Hkv{Hkv}")
+    check_lse(lse, ref_lse)
+
+
 @pytest.mark.parametrize("G", [1, 2, 4])
 def test_empty_requests_in_the_batch(gpu_device, G):
     """Requests with no query rows (q_len = 0) among others get no Q tile, and
