@@ -202,7 +202,6 @@ def main():
               "(o, lse) partials before the merge. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    os.environ["PKV_DECODE_KERNEL"] = args.kernel
     import torch
 
     import paged_kv_gqa_store_amd as pkv
@@ -239,7 +238,8 @@ def main():
         pkv.kv_store(kp, vp, k_new, v_new, slots)
         if ev is not None:
             ev[1].record()
-        pkv.paged_decode_attn(q, kp, vp, page_table, seq_lens, max_len, S, o_partial=o_p, lse_partial=l_p)
+        pkv.paged_decode_attn(q, kp, vp, page_table, seq_lens, max_len, S, o_partial=o_p, lse_partial=l_p,
+                              kernel=args.kernel)
         if ev is not None:
             ev[2].record()
         pkv.decode_merge(o_p, l_p, out=out)
@@ -305,7 +305,7 @@ def main():
         # (rotating pools as above): its average duration for the roofline
         attn_graph_us = time_graph_launches(lambda i: pkv.paged_decode_attn(
             q, pools[i % len(pools)][0], pools[i % len(pools)][1], page_table, seq_lens, max_len, S,
-            o_partial=o_p, lse_partial=l_p), args.steps)
+            o_partial=o_p, lse_partial=l_p, kernel=args.kernel), args.steps)
         achieved = attn_kernel_b / (attn_graph_us * 1e-6) / 1e9
         log(f"[bench] attention kernel alone, {args.steps} launches in one graph: {attn_graph_us:.1f} us per launch, "
             f"{achieved:.0f} GB/s = {achieved / PEAK_HBM_GBPS:.1%} of {PEAK_HBM_GBPS:.0f} GB/s")

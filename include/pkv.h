@@ -9,10 +9,12 @@
  *   pkv_prefill_plan      the Q-tile work map of a prefill batch (host only)
  *   pkv_indexing          row gather from a vocabulary slice (embedding lookup)
  *   pkv_paged_decode_attn split-KV attention through the page table -> partials
+ *   pkv_paged_decode_attn_valu  the same on the vector ALUs only (measured alternative)
  *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
  *   pkv_paged_decode_attn_merged  the attention and the merge in one call
  *   pkv_decode_step       store, attention and merge in one call (one kernel at S = 1)
  *   pkv_num_splits        split-count heuristic (host only)
+ *   pkv_num_splits_batch  the same, given the group size and token count (host only)
  *   pkv_split_chunk       positions per split for a split count (host only)
  *   pkv_status_str        text of a status code
  *
@@ -236,6 +238,24 @@ pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *
                                  float *o_partial, float *lse_partial, void *stream);
 
 /*
+ * pkv_paged_decode_attn_valu -- pkv_paged_decode_attn computed by the all-VALU
+ * kernel instead of the matrix-core one: the same contract, arguments, status
+ * codes and results (up to fp32 summation order), plus num_splits <= 65535.
+ * Kept as the measured alternative of the choice to run QK^T on the matrix
+ * cores (AstrAI "CUDA Kernels", section "File Layout", runs decode on mma
+ * tiles; here the fp32 dot products run on the vector ALUs, one online-softmax
+ * state per token slot, merged at the end).  It is roughly half as fast on
+ * grouped heads and is selected only by calling it.
+ */
+pkv_status pkv_paged_decode_attn_valu(const void *q, const void *k_pool, const void *v_pool,
+                                      const int32_t *page_table, const int32_t *seq_lens,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t page_size, int32_t num_pages,
+                                      int32_t max_pages_per_seq, int32_t max_seq_len,
+                                      int32_t num_splits, float scale, float *o_partial,
+                                      float *lse_partial, void *stream);
+
+/*
  * pkv_decode_merge -- combine the split partials of every (b, h) row.
  *
  * Follows: cuDNN frontend "CSA Fused Compressor", section "ratio=128" (chunked
@@ -301,7 +321,6 @@ pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const
  * Preconditions (device, as in the unfused step): seq_lens[b] >= 1 counts the
  * new token, and slot_mapping[b] is the slot of its position seq_lens[b] - 1
  * (page_table[b][(L-1)/P]*P + (L-1)%P); the slots are distinct.
- * Always runs the matrix-core attention kernel.
  */
 pkv_status pkv_decode_step(const void *q, const void *k_new, const void *v_new,
                            int64_t new_row_stride, const int32_t *slot_mapping, void *k_pool,
@@ -317,22 +336,35 @@ pkv_status pkv_decode_step(const void *q, const void *k_new, const void *v_new,
  * The pages only say the launcher does the split-K arithmetic and that small
  * batches underfill the GPU despite split-KV (AstrAI "CUDA Kernels", sections
  * "File Layout" and "Known Optimization Targets"); the rule is a reading,
- * tuned by measurement on MI355X:
+ * tuned by measurement on MI355X.  This form knows neither the group size nor
+ * the lengths, so it takes the cautious side of pkv_num_splits_batch: one q
+ * head per kv head and a ragged batch,
+ *     pkv_num_splits(B, Hkv, L, P, cus) == pkv_num_splits_batch(B, Hkv, Hkv, L, -1, P, cus)
+ *     = clamp(max(ceil(num_cus / (B * Hkv)), ceil(max_seq_len / 2048)),
+ *             1, min(1024, max(1, ceil(max_seq_len / 256))))
+ * Returns >= 1 for valid arguments, PKV_ERR_SHAPE otherwise (B, Hkv or num_cus
+ * below 1, max_seq_len negative, page_size not a power of two).
+ */
+int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
+                       int32_t num_cus);
+
+/*
+ * pkv_num_splits_batch -- pkv_num_splits for a batch whose group size and
+ * token count the caller knows (a serving scheduler does); host only.
  *     streams = B * Hkv                         one workgroup each per split
  *     S_fill  = ceil(w * num_cus / streams)     w = 2 if Hq/Hkv >= 8, else 1
  *     ragged  = total_tokens < 0 (unknown) or total_tokens < 0.9 * B * max_seq_len
  *     S       = ragged ? max(S_fill, ceil(max_seq_len / 2048)) : S_fill
  *     S       = clamp(S, 1, min(1024, max(1, ceil(max_seq_len / 256))))
- * total_tokens is the sum of the batch's sequence lengths when the caller
- * knows it (a serving scheduler does), else any negative value.  Uniform
- * batches keep one split per (sequence, kv head) while that fills the GPU;
- * ragged ones are cut into splits of at most 2048 positions, so that the
- * workgroups of long sequences are not the last to finish.
- * Returns >= 1 for valid arguments, PKV_ERR_SHAPE otherwise (B, Hkv or num_cus
- * below 1, Hq not a multiple of Hkv, page_size not a power of two).
+ * total_tokens is the sum of the batch's sequence lengths, or any negative
+ * value when unknown.  Uniform batches keep one split per (sequence, kv head)
+ * while that fills the GPU; ragged ones are cut into splits of at most 2048
+ * positions, so that the workgroups of long sequences are not the last to
+ * finish.  Returns as pkv_num_splits (also PKV_ERR_SHAPE when Hq is not a
+ * multiple of Hkv).
  */
-int32_t pkv_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
-                       int64_t total_tokens, int32_t page_size, int32_t num_cus);
+int32_t pkv_num_splits_batch(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
+                             int64_t total_tokens, int32_t page_size, int32_t num_cus);
 
 /*
  * pkv_prefill_plan -- the packed-query work map of a prefill batch (host only).

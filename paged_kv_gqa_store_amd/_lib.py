@@ -33,7 +33,10 @@ SIGNATURES = [
     ("pkv_prefill_plan", _i32, [_p, _i32, _p, _p, _p, _i32]),
     ("pkv_paged_prefill_attn", _i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _i32, _f32, _p, _p, _p]),
-    ("pkv_num_splits", _i32, [_i32, _i32, _i32, _i32, _i64, _i32, _i32]),
+    ("pkv_paged_decode_attn_valu", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _f32, _p, _p, _p]),
+    ("pkv_num_splits", _i32, [_i32, _i32, _i32, _i32, _i32]),
+    ("pkv_num_splits_batch", _i32, [_i32, _i32, _i32, _i32, _i64, _i32, _i32]),
     ("pkv_split_chunk", _i32, [_i32, _i32, _i32]),
     ("pkv_status_str", ctypes.c_char_p, [_i32]),
 ]

@@ -143,8 +143,8 @@ int32_t pkv_prefill_plan(const int32_t *q_lens, int32_t B, int32_t *qo_indptr,
   return t;
 }
 
-int32_t pkv_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
-                       int64_t total_tokens, int32_t page_size, int32_t num_cus) {
+int32_t pkv_num_splits_batch(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
+                             int64_t total_tokens, int32_t page_size, int32_t num_cus) {
   if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || max_seq_len < 0 || !is_pow2(page_size) ||
       num_cus < 1)
     return PKV_ERR_SHAPE;
@@ -161,6 +161,12 @@ int32_t pkv_num_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq_len,
   if (s > cap) s = cap;
   if (s > kMaxSplits) s = kMaxSplits;
   return int32_t(s < 1 ? 1 : s);
+}
+
+int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
+                       int32_t num_cus) {
+  // group size and token count unknown: one q head per kv head, lengths ragged
+  return pkv_num_splits_batch(B, Hkv, Hkv, max_seq_len, -1, page_size, num_cus);
 }
 
 pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_row_stride,
@@ -240,7 +246,24 @@ pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *
                                          page_size, num_pages, max_pages_per_seq, max_seq_len,
                                          num_splits, scale, o_partial, lse_partial, p);
   if (st != PKV_OK || p.B == 0) return st;
-  hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_paged_decode_mfma(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_paged_decode_attn_valu(const void *q, const void *k_pool, const void *v_pool,
+                                      const int32_t *page_table, const int32_t *seq_lens,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t page_size, int32_t num_pages,
+                                      int32_t max_pages_per_seq, int32_t max_seq_len,
+                                      int32_t num_splits, float scale, float *o_partial,
+                                      float *lse_partial, void *stream) {
+  pkv::DecodeParams p;
+  const pkv_status st = attention_params(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D,
+                                         page_size, num_pages, max_pages_per_seq, max_seq_len,
+                                         num_splits, scale, o_partial, lse_partial, p);
+  if (st != PKV_OK || p.B == 0) return st;
+  if (num_splits > 65535) return PKV_ERR_SHAPE;   // grid (splits, kv heads, sequences)
+  hipError_t e = pkv::launch_paged_decode_valu(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -266,7 +289,7 @@ pkv_status pkv_paged_decode_attn_rope(const void *q, const void *k_pool, const v
   p.rope_cos = rope_cos;
   p.rope_sin = rope_sin;
   p.rope_rows = rope_rows;
-  hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_paged_decode_mfma(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -350,7 +373,7 @@ pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const
     p.lse_out = lse_out;
     return pkv::launch_paged_decode_mfma(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
   }
-  if (pkv::launch_paged_decode(p, s) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_paged_decode_mfma(p, s) != hipSuccess) return PKV_ERR_HIP;
   const hipError_t e = pkv::launch_decode_merge(o_partial, lse_partial, B * Hq, D, num_splits,
                                                 static_cast<uint16_t *>(out), lse_out, s);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;

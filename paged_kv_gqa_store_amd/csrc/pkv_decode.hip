@@ -12,8 +12,6 @@
 // One workgroup per (split, kv head, sequence).  Scores are kept in the log2
 // domain: q is pre-multiplied by scale*log2(e), so exp is one v_exp_f32.
 #include <math.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include "pkv_device.h"
 #include "pkv_launch.h"
@@ -230,14 +228,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restri
 }
 
 }  // namespace
-
-hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
-  const char *v = getenv("PKV_DECODE_KERNEL");
-  // the VALU kernel has no rotary-embedding prologue; rotated-q calls always
-  // take the matrix-core kernel
-  if (v && strcmp(v, "valu") == 0 && !p.q_pos) return launch_paged_decode_valu(p, stream);
-  return launch_paged_decode_mfma(p, stream);
-}
 
 hipError_t launch_paged_decode_valu(const DecodeParams &p, hipStream_t stream) {
 #define PKV_CASE(DD, GG) \

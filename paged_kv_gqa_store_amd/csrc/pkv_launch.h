@@ -54,10 +54,9 @@ hipError_t launch_gather_rows(void *out, const void *weight, int64_t length, con
                               int64_t n, int64_t start, int64_t row_b, int unit_b,
                               hipStream_t stream);
 
-// Split-KV decode.  The matrix-core kernel runs by default; PKV_DECODE_KERNEL=valu
-// in the environment selects the all-VALU kernel instead (kept as the measured
-// baseline of that design choice; both honour the same contract).
-hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
+// Split-KV decode: the matrix-core kernel (every decode entry point) and the
+// all-VALU kernel (only pkv_paged_decode_attn_valu, the measured alternative
+// of that design choice; both honour the same contract).
 hipError_t launch_paged_decode_valu(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_paged_decode_mfma(const DecodeParams &p, hipStream_t stream);
 

@@ -44,11 +44,12 @@ def num_cus(device=None) -> int:
 
 def num_splits(B: int, Hq: int, Hkv: int, max_seq_len: int, page_size: int,
                total_tokens: int = -1, n_cus: int | None = None) -> int:
-    """The split-count heuristic of the library (host only).  ``total_tokens``
-    is the sum of the sequence lengths if known (-1: unknown, treated as ragged)."""
+    """The split-count heuristic of the library (host only,
+    ``pkv_num_splits_batch``).  ``total_tokens`` is the sum of the sequence
+    lengths if known (-1: unknown, treated as ragged)."""
     n_cus = num_cus() if n_cus is None else n_cus
-    s = lib().pkv_num_splits(B, Hq, Hkv, max_seq_len, total_tokens, page_size, n_cus)
-    check(min(s, 0), "pkv_num_splits")
+    s = lib().pkv_num_splits_batch(B, Hq, Hkv, max_seq_len, total_tokens, page_size, n_cus)
+    check(min(s, 0), "pkv_num_splits_batch")
     return s
 
 
@@ -227,7 +228,7 @@ def workspace(B: int, Hq: int, D: int, splits: int, device) -> tuple[torch.Tenso
 def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
                       splits: int | None = None, scale: float | None = None,
                       o_partial=None, lse_partial=None, total_tokens: int = -1,
-                      q_positions=None, rope_cos=None, rope_sin=None):
+                      q_positions=None, rope_cos=None, rope_sin=None, kernel: str = "mfma"):
     """Split-KV attention over the paged pool; returns (o_partial, lse_partial).
 
     q ``[B,Hq,D]`` bf16; pools ``[num_pages,P,Hkv,D]`` bf16; page_table int32
@@ -236,7 +237,10 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
     the caller knows it) only steers the split heuristic when ``splits`` is None.
     With ``q_positions`` (int32 ``[B]``) and fp32 ``rope_cos``/``rope_sin``
     ``[rows, D/2]``, q is rotated by the rotary embedding in the kernel's
-    prologue (``pkv_paged_decode_attn_rope``)."""
+    prologue (``pkv_paged_decode_attn_rope``).  ``kernel="valu"`` calls the
+    all-VALU kernel (``pkv_paged_decode_attn_valu``, no rotary prologue)."""
+    _require(kernel in ("mfma", "valu"), "kernel must be 'mfma' or 'valu'")
+    _require(kernel == "mfma" or q_positions is None, "the VALU kernel has no rotary prologue")
     _on_gpu(q, k_pool, v_pool, page_table, seq_lens)
     _require(q.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16,
              "q and the pools must be bfloat16")
@@ -260,7 +264,10 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
     args = (q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), page_table.data_ptr(),
             seq_lens.data_ptr(), B, Hq, Hkv, D, P, num_pages, page_table.shape[1], max_seq_len, S,
             scale, o_partial.data_ptr(), lse_partial.data_ptr())
-    if q_positions is None:
+    if kernel == "valu":
+        st = lib().pkv_paged_decode_attn_valu(*args, _stream(q))
+        check(st, "pkv_paged_decode_attn_valu")
+    elif q_positions is None:
         st = lib().pkv_paged_decode_attn(*args, _stream(q))
         check(st, "pkv_paged_decode_attn")
     else:

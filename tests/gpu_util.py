@@ -36,9 +36,10 @@ def host_f64_from_bf16(t: torch.Tensor) -> np.ndarray:
 class DeviceStep:
     """One decode step's inputs resident on the GPU."""
 
-    def __init__(self, inp: W.Inputs, dev, pools=None, page_table=None):
+    def __init__(self, inp: W.Inputs, dev, pools=None, page_table=None, kernel: str = "mfma"):
         self.inp = inp
         self.dev = dev
+        self.kernel = kernel
         k_pool, v_pool = (inp.k_pool, inp.v_pool) if pools is None else pools
         self.q = bf16_dev(inp.q, dev)
         self.k_pool = bf16_dev(k_pool, dev)
@@ -55,7 +56,7 @@ class DeviceStep:
     def attend(self, splits=None, want_lse=False):
         o_p, l_p = pkv.paged_decode_attn(self.q, self.k_pool, self.v_pool, self.page_table,
                                          self.seq_lens, self.inp.max_seq_len, splits,
-                                         total_tokens=int(self.inp.seq_lens.sum()))
+                                         total_tokens=int(self.inp.seq_lens.sum()), kernel=self.kernel)
         res = pkv.decode_merge(o_p, l_p, want_lse=want_lse)
         return res, o_p, l_p
 

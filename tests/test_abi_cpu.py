@@ -28,17 +28,29 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(["pkv_kv_store", "pkv_paged_decode_attn", "pkv_decode_merge",
-                                         "pkv_num_splits", "pkv_split_chunk", "pkv_status_str",
-                                         "pkv_indexing", "pkv_kv_store_rope",
-                                         "pkv_paged_decode_attn_rope", "pkv_prefill_plan",
-                                         "pkv_paged_prefill_attn", "pkv_paged_decode_attn_merged",
-                                         "pkv_decode_step"])
+                                         "pkv_num_splits", "pkv_num_splits_batch", "pkv_split_chunk",
+                                         "pkv_status_str", "pkv_indexing", "pkv_kv_store_rope",
+                                         "pkv_paged_decode_attn_rope", "pkv_paged_decode_attn_valu",
+                                         "pkv_prefill_plan", "pkv_paged_prefill_attn",
+                                         "pkv_paged_decode_attn_merged", "pkv_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_symbols():
         assert hasattr(lib, name), name
     assert {s[0] for s in _lib.SIGNATURES} == set(declared_symbols())
+
+
+def test_contracted_split_count_signature():
+    """pkv_num_splits takes (B, Hkv, max_seq_len, page_size, num_cus), as the
+    boundary contract states; the form with the group size and token count is
+    pkv_num_splits_batch."""
+    decl = re.search(r"int32_t pkv_num_splits\((.*?)\);", HEADER, flags=re.S).group(1)
+    names = [a.split()[-1] for a in decl.replace("\n", " ").split(",")]
+    assert names == ["B", "Hkv", "max_seq_len", "page_size", "num_cus"]
+    decl = re.search(r"int32_t pkv_num_splits_batch\((.*?)\);", HEADER, flags=re.S).group(1)
+    names = [a.split()[-1] for a in decl.replace("\n", " ").split(",")]
+    assert names == ["B", "Hq", "Hkv", "max_seq_len", "total_tokens", "page_size", "num_cus"]
 
 
 def test_status_strings(lib):
@@ -54,10 +66,28 @@ def test_split_heuristic_on_the_five_workloads(lib):
              (4, 64, 8, 65536, 4 * 65536, 16): 16,  # uniform, G = 8: two workgroups per CU
              (128, 16, 16, 2048, 128 * 2048, 1): 1}
     for args, s in cases.items():
-        assert lib.pkv_num_splits(*args, 256) == s, args
+        assert lib.pkv_num_splits_batch(*args, 256) == s, args
     # the same shapes without a token count are treated as ragged
-    assert lib.pkv_num_splits(32, 32, 8, 4096, -1, 16, 256) == 2
-    assert lib.pkv_num_splits(4, 64, 8, 65536, -1, 16, 256) == 32
+    assert lib.pkv_num_splits_batch(32, 32, 8, 4096, -1, 16, 256) == 2
+    assert lib.pkv_num_splits_batch(4, 64, 8, 65536, -1, 16, 256) == 32
+
+
+def test_contracted_split_count_is_the_cautious_batch_form(lib):
+    """Without Hq and the token count: one q head per kv head, ragged lengths."""
+    for B in [1, 2, 4, 32, 64, 128, 500]:
+        for Hkv in [1, 8, 16]:
+            for L in [0, 1, 100, 255, 256, 2049, 4096, 8192, 65536, 100000]:
+                for P in [1, 16]:
+                    s = lib.pkv_num_splits(B, Hkv, L, P, 256)
+                    assert s == lib.pkv_num_splits_batch(B, Hkv, Hkv, L, -1, P, 256)
+                    cap = min(1024, max(1, -(-L // 256)))
+                    assert s == max(1, min(cap, max(-(-256 // (B * Hkv)), -(-L // 2048))))
+    assert lib.pkv_num_splits(32, 8, 4096, 16, 256) == 2
+    assert lib.pkv_num_splits(0, 8, 10, 16, 256) == SHAPE
+    assert lib.pkv_num_splits(1, 0, 10, 16, 256) == SHAPE
+    assert lib.pkv_num_splits(1, 8, -1, 16, 256) == SHAPE
+    assert lib.pkv_num_splits(1, 8, 10, 12, 256) == SHAPE
+    assert lib.pkv_num_splits(1, 8, 10, 16, 0) == SHAPE
 
 
 def test_split_heuristic_properties(lib):
@@ -66,13 +96,13 @@ def test_split_heuristic_properties(lib):
             for L in [0, 1, 255, 256, 2049, 100000]:
                 cap = max(1, -(-L // 256))
                 for total in [-1, B * L, B * L // 2]:
-                    s = lib.pkv_num_splits(B, Hq, Hkv, L, total, 16, 256)
+                    s = lib.pkv_num_splits_batch(B, Hq, Hkv, L, total, 16, 256)
                     assert 1 <= s <= min(cap, 1024)
                     if L > 0 and (total < 0 or 10 * total < 9 * B * L):
                         assert s >= min(-(-L // 2048), cap)
-    assert lib.pkv_num_splits(0, 8, 8, 10, -1, 16, 256) == SHAPE
-    assert lib.pkv_num_splits(1, 8, 8, 10, -1, 12, 256) == SHAPE
-    assert lib.pkv_num_splits(1, 12, 8, 10, -1, 16, 256) == SHAPE
+    assert lib.pkv_num_splits_batch(0, 8, 8, 10, -1, 16, 256) == SHAPE
+    assert lib.pkv_num_splits_batch(1, 8, 8, 10, -1, 12, 256) == SHAPE
+    assert lib.pkv_num_splits_batch(1, 12, 8, 10, -1, 16, 256) == SHAPE
 
 
 def test_split_chunk_agrees_with_the_oracle_reading(lib):
@@ -140,30 +170,34 @@ def test_prefill_plan_reproduces_the_worked_example(lib):
     assert tb[:3].tolist() == [1, 2, 2] and ti[:3].tolist() == [0, 0, 1]
 
 
-def _attn(lib, **kw):
+def _attn(lib, fn="pkv_paged_decode_attn", **kw):
     p = ctypes.c_void_p(256)
     a = dict(q=p, k=p, v=p, pt=p, sl=p, B=2, Hq=8, Hkv=2, D=128, P=16, pages=10, mp=4, L=64, S=2,
              scale=0.088, o=p, lse=p)
     a.update(kw)
-    return lib.pkv_paged_decode_attn(a["q"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["Hq"], a["Hkv"],
-                                     a["D"], a["P"], a["pages"], a["mp"], a["L"], a["S"], a["scale"],
-                                     a["o"], a["lse"], None)
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["Hq"], a["Hkv"],
+                            a["D"], a["P"], a["pages"], a["mp"], a["L"], a["S"], a["scale"],
+                            a["o"], a["lse"], None)
 
 
-def test_attention_validation(lib):
-    assert _attn(lib, B=0) == OK
-    assert _attn(lib, q=None) == NULL
-    assert _attn(lib, lse=None) == NULL
-    assert _attn(lib, Hq=7) == SHAPE
-    assert _attn(lib, D=96) == UNSUP
-    assert _attn(lib, Hq=32) == UNSUP            # G = 16
-    assert _attn(lib, P=12) == UNSUP
-    assert _attn(lib, L=65) == SHAPE             # beyond max_pages * P
-    assert _attn(lib, S=0) == SHAPE
-    assert _attn(lib, S=1025) == SHAPE
-    assert _attn(lib, scale=0.0) == SHAPE
-    assert _attn(lib, q=ctypes.c_void_p(258)) == ALIGN
-    assert _attn(lib, k=ctypes.c_void_p(264)) == ALIGN
+@pytest.mark.parametrize("fn", ["pkv_paged_decode_attn", "pkv_paged_decode_attn_valu"])
+def test_attention_validation(lib, fn):
+    def attn(lib, **kw):
+        return _attn(lib, fn, **kw)
+
+    assert attn(lib, B=0) == OK
+    assert attn(lib, q=None) == NULL
+    assert attn(lib, lse=None) == NULL
+    assert attn(lib, Hq=7) == SHAPE
+    assert attn(lib, D=96) == UNSUP
+    assert attn(lib, Hq=32) == UNSUP            # G = 16
+    assert attn(lib, P=12) == UNSUP
+    assert attn(lib, L=65) == SHAPE             # beyond max_pages * P
+    assert attn(lib, S=0) == SHAPE
+    assert attn(lib, S=1025) == SHAPE
+    assert attn(lib, scale=0.0) == SHAPE
+    assert attn(lib, q=ctypes.c_void_p(258)) == ALIGN
+    assert attn(lib, k=ctypes.c_void_p(264)) == ALIGN
 
 
 def _merged(lib, out=ctypes.c_void_p(256), lse_out=None, **kw):

@@ -18,10 +18,10 @@ pytestmark = pytest.mark.gpu
 _cache = {}
 
 
-@pytest.fixture(autouse=True, params=["mfma", "valu"])
-def decode_kernel(request, monkeypatch):
-    """Every test runs on both decode kernels (matrix-core default and all-VALU)."""
-    monkeypatch.setenv("PKV_DECODE_KERNEL", request.param)
+@pytest.fixture(params=["mfma", "valu"])
+def decode_kernel(request):
+    """Every test runs on both decode kernels: the matrix-core one behind every
+    decode entry point, and the all-VALU one (pkv_paged_decode_attn_valu)."""
     return request.param
 
 
@@ -38,12 +38,12 @@ def _oracle_full(inp):
 
 
 @pytest.mark.parametrize("wl", ["tiny_gqa", "llama3_8b_decode", "ragged_batch", "long_context", "mha_page1"])
-def test_decode_step_matches_oracle(gpu_device, wl):
+def test_decode_step_matches_oracle(gpu_device, decode_kernel, wl):
     inp = inputs(wl)
     S = pkv.num_splits(inp.cfg.B, inp.cfg.Hq, inp.cfg.Hkv, inp.max_seq_len, inp.cfg.P,
                        int(inp.seq_lens.sum()))
     print(f"decode step {wl} ({inp.cfg.describe()}), num_splits {S}", flush=True)
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     (out, lse), o_p, l_p = st.step(want_lse=True)
     torch.cuda.synchronize()
     ref, ref_lse = _oracle_full(inp)
@@ -58,13 +58,13 @@ def test_decode_step_matches_oracle(gpu_device, wl):
 
 
 @pytest.mark.parametrize("wl", ["tiny_gqa", "llama3_8b_decode", "long_context"])
-def test_partials_match_oracle_split_mode(gpu_device, wl):
+def test_partials_match_oracle_split_mode(gpu_device, decode_kernel, wl):
     inp = inputs(wl)
     cfg = inp.cfg
     S = pkv.num_splits(cfg.B, cfg.Hq, cfg.Hkv, inp.max_seq_len, cfg.P, int(inp.seq_lens.sum()))
     if wl in ("tiny_gqa", "llama3_8b_decode"):
         S = 3 if wl == "tiny_gqa" else 2  # force several splits where the heuristic picks one
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     st.store()
     _, o_p, l_p = st.attend(splits=S)
     torch.cuda.synchronize()
@@ -100,10 +100,10 @@ def test_merge_alone_on_oracle_partials(gpu_device):
     assert np.abs(lse.cpu().numpy() - lse_ref).max() <= 1e-5 * max(1, np.abs(lse_ref).max())
 
 
-def test_length_one_returns_the_value_row_bit_exact(gpu_device):
+def test_length_one_returns_the_value_row_bit_exact(gpu_device, decode_kernel):
     cfg = W.custom_config(B=5, Hq=16, Hkv=2, D=128, P=16, num_pages=12, seq_lens=(1,) * 5)
     inp = W.make_inputs(cfg)
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     out, _, _ = st.step(splits=3)
     torch.cuda.synchronize()
     got = host_u16(out)
@@ -114,7 +114,7 @@ def test_length_one_returns_the_value_row_bit_exact(gpu_device):
             assert (got[b, h] == vf[page, 0, h // 8]).all()
 
 
-def test_identical_keys_give_mean_of_values(gpu_device):
+def test_identical_keys_give_mean_of_values(gpu_device, decode_kernel):
     cfg = W.custom_config(B=3, Hq=8, Hkv=2, D=64, P=16, num_pages=40, seq_lens=(5, 300, 129))
     inp = W.make_inputs(cfg)
     kf, vf = inp.pools_after_store()
@@ -122,7 +122,7 @@ def test_identical_keys_give_mean_of_values(gpu_device):
     kp = inp.k_pool.copy()
     kp[:] = key
     knew = np.tile(key.reshape(1, -1), (3, 1))
-    st = DeviceStep(inp, gpu_device, pools=(kp, inp.v_pool))
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel, pools=(kp, inp.v_pool))
     st.k_new = bf16_dev(knew, gpu_device)
     out, _, _ = st.step(splits=2)
     torch.cuda.synchronize()
@@ -137,20 +137,20 @@ def test_identical_keys_give_mean_of_values(gpu_device):
 
 
 @pytest.mark.parametrize("wl", ["tiny_gqa", "ragged_batch"])
-def test_paged_equals_contiguous_bitwise(gpu_device, wl):
+def test_paged_equals_contiguous_bitwise(gpu_device, decode_kernel, wl):
     inp = inputs(wl)
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     out1, _, _ = st.step()
     kc, vc, ptc = W.contiguous_layout(inp)
-    st2 = DeviceStep(inp, gpu_device, pools=(kc, vc), page_table=ptc)
+    st2 = DeviceStep(inp, gpu_device, kernel=decode_kernel, pools=(kc, vc), page_table=ptc)
     out2, _, _ = st2.attend()
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
 
 
-def test_run_to_run_determinism(gpu_device):
+def test_run_to_run_determinism(gpu_device, decode_kernel):
     inp = inputs("llama3_8b_decode")
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     st.store()
     a, _, _ = st.attend()
     b, _, _ = st.attend()
@@ -158,19 +158,19 @@ def test_run_to_run_determinism(gpu_device):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_split_count_invariance(gpu_device):
+def test_split_count_invariance(gpu_device, decode_kernel):
     """S = 1 and S = k agree to within one bf16 rounding step."""
     inp = inputs("llama3_8b_decode")
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     st.store()
     outs = [host_f64_from_bf16(st.attend(splits=s)[0]) for s in (1, 2, 5, 16)]
     for o in outs[1:]:
         assert (np.abs(o - outs[0]) <= np.abs(outs[0]) * 2.0 ** -7 + 1e-6).all()
 
 
-def test_value_scaling_by_power_of_two_is_exact(gpu_device):
+def test_value_scaling_by_power_of_two_is_exact(gpu_device, decode_kernel):
     inp = inputs("tiny_gqa")
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     out1, _, _ = st.step(splits=2)
     st.v_pool.mul_(2.0 ** 5)
     out2, _, _ = st.attend(splits=2)
@@ -180,14 +180,14 @@ def test_value_scaling_by_power_of_two_is_exact(gpu_device):
 
 @pytest.mark.parametrize("D,G,P", [(64, 1, 1), (64, 2, 2), (64, 8, 64), (128, 1, 16), (128, 2, 4),
                                    (128, 4, 1), (128, 8, 16), (128, 8, 256), (64, 4, 1024)])
-def test_shapes_and_ragged_tails(gpu_device, D, G, P):
+def test_shapes_and_ragged_tails(gpu_device, decode_kernel, D, G, P):
     Hkv = 2
     lens = (1, P - 1 if P > 1 else 1, P, 3 * P + 1, 777, 1500)
     cfg = W.custom_config(name=f"d{D}g{G}p{P}", B=len(lens), Hq=G * Hkv, Hkv=Hkv, D=D, P=P,
                           num_pages=-(-sum(lens) // P) + len(lens) + 3, seq_lens=lens)
     inp = W.make_inputs(cfg)
     for S in (1, 3):
-        st = DeviceStep(inp, gpu_device)
+        st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
         out, _, _ = st.step(splits=S)
         torch.cuda.synchronize()
         check_attention(out, _oracle_full(inp)[0], f"D{D} G{G} P{P} S{S}")
@@ -198,25 +198,26 @@ def test_shapes_and_ragged_tails(gpu_device, D, G, P):
     (64, 1, 1, (4097,), 2),               # two splits of 2049 pages: each past one segment
     (128, 4, 16, (40000, 33000), 1),      # 2500 and 2063 pages: two segments each
 ])
-def test_splits_longer_than_one_page_id_segment(gpu_device, D, G, P, lens, S):
+def test_splits_longer_than_one_page_id_segment(gpu_device, decode_kernel, D, G, P, lens, S):
     """A split whose pages exceed the 2048 page ids staged in LDS at a time
     refetches them segment by segment."""
     cfg = W.custom_config(name=f"long_split_d{D}g{G}p{P}", B=len(lens), Hq=G, Hkv=1, D=D, P=P,
                           num_pages=-(-sum(lens) // P) + len(lens) + 3, seq_lens=lens)
     inp = W.make_inputs(cfg)
     print(f"long splits D{D} G{G} P{P} lens {lens} S{S}", flush=True)
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     out, _, _ = st.step(splits=S)
     torch.cuda.synchronize()
     check_attention(out, _oracle_full(inp)[0], f"long splits D{D} G{G} P{P} S{S}")
 
 
-def test_empty_sequence_and_empty_splits(gpu_device):
+def test_empty_sequence_and_empty_splits(gpu_device, decode_kernel):
     cfg = W.custom_config(B=3, Hq=4, Hkv=1, D=64, P=16, num_pages=20, seq_lens=(0, 3, 200))
     inp = W.make_inputs(cfg)
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     st.store()
-    o_p, l_p = pkv.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, 200, 7)
+    o_p, l_p = pkv.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, 200, 7,
+                                     kernel=decode_kernel)
     out, lse = pkv.decode_merge(o_p, l_p, want_lse=True)
     torch.cuda.synchronize()
     g = host_f64_from_bf16(out)
@@ -226,53 +227,56 @@ def test_empty_sequence_and_empty_splits(gpu_device):
     check_attention(out[1:], ref[1:], "nonempty rows")
 
 
-def test_canary_reaches_output_when_store_is_skipped(gpu_device):
+def test_canary_reaches_output_when_store_is_skipped(gpu_device, decode_kernel):
     inp = inputs("tiny_gqa")
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     out, _, _ = st.attend()
     torch.cuda.synchronize()
     assert torch.isnan(out.float()).all()
 
 
-def test_bad_page_id_poisons_only_its_row(gpu_device):
+def test_bad_page_id_poisons_only_its_row(gpu_device, decode_kernel):
     inp = inputs("tiny_gqa")
     pt = inp.page_table.copy()
     pt[1, 2] = inp.cfg.num_pages + 5
-    st = DeviceStep(inp, gpu_device, page_table=pt)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel, page_table=pt)
     out, _, _ = st.step()
     torch.cuda.synchronize()
     o = out.float().cpu()
     assert torch.isnan(o[1]).all() and torch.isfinite(o[0]).all()
 
 
-def test_max_splits(gpu_device):
+def test_max_splits(gpu_device, decode_kernel):
     cfg = W.custom_config(B=1, Hq=8, Hkv=1, D=128, P=1, num_pages=3000, seq_lens=(2049,))
     inp = W.make_inputs(cfg)
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     out, o_p, _ = st.step(splits=1024)
     torch.cuda.synchronize()
     assert o_p.shape[2] == 1024
     check_attention(out, _oracle_full(inp)[0], "S=1024")
 
 
-def test_errors_raise(gpu_device):
+def test_errors_raise(gpu_device, decode_kernel):
     inp = inputs("tiny_gqa")
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     with pytest.raises(RuntimeError):
-        pkv.paged_decode_attn(st.q.float(), st.k_pool, st.v_pool, st.page_table, st.seq_lens, 100)
+        pkv.paged_decode_attn(st.q.float(), st.k_pool, st.v_pool, st.page_table, st.seq_lens, 100,
+                              kernel=decode_kernel)
     with pytest.raises(RuntimeError):   # max_seq_len beyond max_pages * page_size
-        pkv.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, 10_000)
+        pkv.paged_decode_attn(st.q, st.k_pool, st.v_pool, st.page_table, st.seq_lens, 10_000,
+                              kernel=decode_kernel)
     with pytest.raises(RuntimeError):
         q_bad = torch.empty(st.q.numel() + 8, dtype=torch.bfloat16, device=gpu_device)[1:1 + st.q.numel()]
-        pkv.paged_decode_attn(q_bad.view(st.q.shape), st.k_pool, st.v_pool, st.page_table, st.seq_lens, 100)
+        pkv.paged_decode_attn(q_bad.view(st.q.shape), st.k_pool, st.v_pool, st.page_table, st.seq_lens, 100,
+                              kernel=decode_kernel)
 
 
-def test_nan_query_gives_nan_rows(gpu_device):
+def test_nan_query_gives_nan_rows(gpu_device, decode_kernel):
     """Every score of a row NaN: the row is NaN (as in the oracle), not an empty split's zeros."""
     inp = inputs("tiny_gqa")
     q = inp.q.copy()
     q[1, 2] = W.BF16_NAN
-    st = DeviceStep(inp, gpu_device)
+    st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     st.q = bf16_dev(q, gpu_device)
     (out, lse), _, _ = st.step(splits=3, want_lse=True)
     torch.cuda.synchronize()
