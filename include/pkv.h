@@ -12,6 +12,7 @@
  *   pkv_paged_decode_attn_valu  the same on the vector ALUs only (measured alternative)
  *   pkv_decode_merge      log-sum-exp merge of the partials -> bf16 output
  *   pkv_paged_decode_attn_merged  the attention and the merge in one call
+ *   pkv_paged_decode_attn_merged_static  the same without workspace or allocation
  *   pkv_decode_step       store, attention and merge in one call (one kernel at S = 1)
  *   pkv_num_splits        split-count heuristic (host only)
  *   pkv_num_splits_batch  the same, given the group size and token count (host only)
@@ -20,7 +21,8 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are device pointers unless stated; every buffer belongs to the
- *     caller.  The library never allocates, frees or synchronises: each call
+ *     caller.  The library never allocates, frees or synchronises (its one
+ *     static array is described at pkv_paged_decode_attn_merged_static): each call
  *     validates its arguments on the host, enqueues its kernels on `stream`
  *     (a hipStream_t; NULL = the default stream) and returns.
  *   - A negative status means that nothing was launched (except PKV_ERR_HIP,
@@ -56,6 +58,7 @@ typedef int32_t pkv_status;
 #define PKV_ERR_UNSUPPORTED (-3) /* head_dim / group size / page size not supported  */
 #define PKV_ERR_ALIGN (-4)       /* a base pointer or stride is not 16-byte aligned  */
 #define PKV_ERR_HIP (-5)         /* the HIP runtime reported a launch failure        */
+#define PKV_ERR_SCRATCH (-6)     /* the partials do not fit the static scratch buffer */
 
 /*
  * pkv_kv_store -- write n new rows into the K and V pools by slot index.
@@ -296,6 +299,36 @@ pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const
                                         int32_t num_splits, float scale, float *o_partial,
                                         float *lse_partial, void *out, float *lse_out,
                                         void *stream);
+
+/*
+ * pkv_paged_decode_attn_merged_static -- pkv_paged_decode_attn_merged with no
+ * workspace argument and no allocation of any kind, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  With num_splits > 1 the split partials go
+ * to a static device array of the library (16 MiB, one copy per GPU, held
+ * until the process ends) instead of caller buffers; the kernels, and so the
+ * out / lse_out bits, are those of pkv_paged_decode_attn_merged.
+ *   Arguments as pkv_paged_decode_attn_merged without o_partial / lse_partial.
+ *   Limit: B * Hq * num_splits * D floats, rounded up to a multiple of 64,
+ *   plus B * Hq * num_splits floats must not exceed 4 Mi (16 MiB); otherwise
+ *   PKV_ERR_SCRATCH and nothing is launched.  num_splits == 1 uses no scratch.
+ *   The array of a GPU is found (hipGetSymbolAddress) on the first call on
+ *   that GPU, which must be the GPU current on the calling thread and the
+ *   stream's; later calls only launch.
+ *   Every call on one GPU shares that GPU's array, and the attention writes
+ *   every partial before the merge reads it, so nothing needs clearing between
+ *   calls; calls whose kernels overlap on one GPU (other streams, other
+ *   threads) race on it and must be serialised by the caller.
+ * Status codes as pkv_paged_decode_attn_merged, plus PKV_ERR_SCRATCH.
+ */
+pkv_status pkv_paged_decode_attn_merged_static(const void *q, const void *k_pool,
+                                               const void *v_pool, const int32_t *page_table,
+                                               const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                               int32_t Hkv, int32_t D, int32_t page_size,
+                                               int32_t num_pages, int32_t max_pages_per_seq,
+                                               int32_t max_seq_len, int32_t num_splits,
+                                               float scale, void *out, float *lse_out,
+                                               void *stream);
 
 /*
  * pkv_decode_step -- one whole decode step: pkv_kv_store of one new row per

@@ -8,8 +8,10 @@ One decode step is three hand-written HIP kernels behind a C ABI
 * ``decode_merge``       log-sum-exp merge of the split partials;
 
 (``paged_decode_attn_merged`` runs the last two as one call: a single kernel
-when there is one split; ``decode_step_fused`` runs all three as one call,
-the store fused into the attention kernel),
+when there is one split; ``paged_decode_attn_merged_static`` does the same
+with its partials in a static device array, allocating nothing;
+``decode_step_fused`` runs all three as one call, the store fused into the
+attention kernel),
 
 plus ``paged_prefill_attn`` (packed multi-token queries over the same pool,
 with the ``prefill_plan`` work map), ``kv_store_rope`` (the store with K rotated by a rotary embedding on the
@@ -25,6 +27,6 @@ fallback implementation.
 """
 from .ops import (  # noqa: F401
     PrefillPlan, decode_merge, decode_step, decode_step_fused, indexing, kv_store, kv_store_rope, num_splits,
-    paged_decode_attn, paged_decode_attn_merged, paged_prefill_attn, prefill_plan, split_chunk,
-    workspace,
+    paged_decode_attn, paged_decode_attn_merged, paged_decode_attn_merged_static, paged_prefill_attn,
+    prefill_plan, split_chunk, workspace,
 )

@@ -30,6 +30,8 @@ SIGNATURES = [
                                _i32, _i32, _i32, _f32, _p, _p, _p, _p, _p]),
     ("pkv_paged_decode_attn_merged", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                             _i32, _i32, _f32, _p, _p, _p, _p, _p]),
+    ("pkv_paged_decode_attn_merged_static", _i32, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                   _i32, _i32, _i32, _f32, _p, _p, _p]),
     ("pkv_prefill_plan", _i32, [_p, _i32, _p, _p, _p, _i32]),
     ("pkv_paged_prefill_attn", _i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _i32, _i32, _f32, _p, _p, _p]),

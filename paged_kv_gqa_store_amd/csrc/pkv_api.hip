@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "pkv.h"
 #include "pkv_launch.h"
@@ -94,6 +95,53 @@ pkv_status rope_table_check(const float *rope_cos, const float *rope_sin, int32_
   return PKV_OK;
 }
 
+// Split partials of pkv_paged_decode_attn_merged_static, for callers that
+// cannot allocate: one copy of this array per GPU, alive until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// is a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device, on that entry point's first call there.
+constexpr int64_t kScratchFloats = int64_t(4) << 20;   // 16 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+float *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this GPU's scratch (the GPU current on the calling thread).
+hipError_t scratch_of_current_device(float **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void *a = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<float *>(a) : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (!g_scratch_ptr[dev]) return hipErrorInvalidSymbol;
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// The attention and, with several splits, the merge of the partials p points
+// to; out and lse_out already validated.
+pkv_status launch_merged(pkv::DecodeParams &p, void *out, float *lse_out, hipStream_t s) {
+  if (p.num_splits == 1) {
+    p.out = static_cast<uint16_t *>(out);
+    p.lse_out = lse_out;
+    p.o_partial = nullptr;
+    p.lse_partial = nullptr;
+    return pkv::launch_paged_decode_mfma(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  }
+  if (pkv::launch_paged_decode_mfma(p, s) != hipSuccess) return PKV_ERR_HIP;
+  const hipError_t e = pkv::launch_decode_merge(p.o_partial, p.lse_partial, p.B * p.Hq, p.D,
+                                                p.num_splits, static_cast<uint16_t *>(out),
+                                                lse_out, s);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +154,9 @@ const char *pkv_status_str(pkv_status s) {
     case PKV_ERR_UNSUPPORTED: return "pkv: head_dim, group size or page size not supported";
     case PKV_ERR_ALIGN: return "pkv: a base pointer or stride is not 16-byte aligned";
     case PKV_ERR_HIP: return "pkv: HIP launch failed";
+    case PKV_ERR_SCRATCH:
+      return "pkv: the split partials exceed the 16 MiB static scratch buffer "
+             "(B * Hq * num_splits * (D + 1) floats, plus alignment)";
     default: return "pkv: unknown status";
   }
 }
@@ -367,16 +418,37 @@ pkv_status pkv_paged_decode_attn_merged(const void *q, const void *k_pool, const
   if (!aligned16(out)) return PKV_ERR_ALIGN;
   if (int64_t(B) * Hq > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
   if (!one && !aligned16(o_partial)) return PKV_ERR_ALIGN;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (one) {
-    p.out = static_cast<uint16_t *>(out);
-    p.lse_out = lse_out;
-    return pkv::launch_paged_decode_mfma(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return launch_merged(p, out, lse_out, static_cast<hipStream_t>(stream));
+}
+
+pkv_status pkv_paged_decode_attn_merged_static(const void *q, const void *k_pool,
+                                               const void *v_pool, const int32_t *page_table,
+                                               const int32_t *seq_lens, int32_t B, int32_t Hq,
+                                               int32_t Hkv, int32_t D, int32_t page_size,
+                                               int32_t num_pages, int32_t max_pages_per_seq,
+                                               int32_t max_seq_len, int32_t num_splits,
+                                               float scale, void *out, float *lse_out,
+                                               void *stream) {
+  pkv::DecodeParams p;
+  pkv_status st = attention_params(q, k_pool, v_pool, page_table, seq_lens, B, Hq, Hkv, D,
+                                   page_size, num_pages, max_pages_per_seq, max_seq_len,
+                                   num_splits, scale, nullptr, nullptr, p, false);
+  if (st != PKV_OK || p.B == 0) return st;
+  if (!out) return PKV_ERR_NULL;
+  if (!aligned16(out)) return PKV_ERR_ALIGN;
+  if (int64_t(B) * Hq > (int64_t(1) << 30)) return PKV_ERR_SHAPE;
+  if (num_splits > 1) {
+    // o [B, Hq, S, D] from the start of the array, lse [B, Hq, S] from the next
+    // 256-byte boundary after it
+    const int64_t rows = int64_t(B) * Hq * num_splits;
+    const int64_t lse_off = (rows * D + 63) / 64 * 64;
+    if (lse_off + rows > kScratchFloats) return PKV_ERR_SCRATCH;
+    float *base = nullptr;
+    if (scratch_of_current_device(&base) != hipSuccess) return PKV_ERR_HIP;
+    p.o_partial = base;
+    p.lse_partial = base + lse_off;
   }
-  if (pkv::launch_paged_decode_mfma(p, s) != hipSuccess) return PKV_ERR_HIP;
-  const hipError_t e = pkv::launch_decode_merge(o_partial, lse_partial, B * Hq, D, num_splits,
-                                                static_cast<uint16_t *>(out), lse_out, s);
-  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return launch_merged(p, out, lse_out, static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_decode_step(const void *q, const void *k_new, const void *v_new,

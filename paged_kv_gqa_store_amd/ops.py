@@ -283,7 +283,7 @@ def paged_decode_attn(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
 
 
 def _merged_args(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits, scale, out, lse_out,
-                 want_lse, o_partial, lse_partial, total_tokens):
+                 want_lse, o_partial, lse_partial, total_tokens, partials: bool = True):
     """Checks shared by the calls that end in the merged bf16 output; returns
     the marshalled attention arguments, out and lse_out."""
     _on_gpu(q, k_pool, v_pool, page_table, seq_lens)
@@ -299,7 +299,7 @@ def _merged_args(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits, s
     num_pages, P, Hkv, D2 = k_pool.shape
     _require(D2 == D and page_table.shape[0] == B and seq_lens.shape == (B,), "inconsistent shapes")
     S = num_splits(B, Hq, Hkv, max_seq_len, P, total_tokens) if splits is None else splits
-    if S > 1 and (o_partial is None or lse_partial is None):
+    if partials and S > 1 and (o_partial is None or lse_partial is None):
         o_partial, lse_partial = workspace(B, Hq, D, S, q.device)
     if o_partial is not None:
         _require(o_partial.shape == (B, Hq, S, D) and o_partial.dtype == torch.float32
@@ -337,6 +337,22 @@ def paged_decode_attn_merged(q, k_pool, v_pool, page_table, seq_lens, max_seq_le
     st = lib().pkv_paged_decode_attn_merged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), *tail,
                                             _stream(q))
     check(st, "pkv_paged_decode_attn_merged")
+    return (out, lse_out) if (want_lse or lse_out is not None) else out
+
+
+def paged_decode_attn_merged_static(q, k_pool, v_pool, page_table, seq_lens, max_seq_len: int,
+                                    splits: int | None = None, scale: float | None = None, out=None,
+                                    lse_out=None, want_lse: bool = False, total_tokens: int = -1):
+    """:func:`paged_decode_attn_merged` with the split partials in the
+    library's static device scratch (``pkv_paged_decode_attn_merged_static``):
+    the C call allocates nothing.  Pass ``out`` (and ``lse_out``) to allocate
+    nothing here either.  Calls on one GPU share the scratch: do not let them
+    overlap on different streams."""
+    tail, out, lse_out = _merged_args(q, k_pool, v_pool, page_table, seq_lens, max_seq_len, splits, scale,
+                                      out, lse_out, want_lse, None, None, total_tokens, partials=False)
+    st = lib().pkv_paged_decode_attn_merged_static(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                                   *tail[:12], *tail[14:], _stream(q))
+    check(st, "pkv_paged_decode_attn_merged_static")
     return (out, lse_out) if (want_lse or lse_out is not None) else out
 
 

@@ -14,7 +14,7 @@ from paged_kv_gqa_store_amd import _lib
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = (ROOT / "include" / "pkv.h").read_text()
 
-OK, NULL, SHAPE, UNSUP, ALIGN = 0, -1, -2, -3, -4
+OK, NULL, SHAPE, UNSUP, ALIGN, SCRATCH = 0, -1, -2, -3, -4, -6
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
                                          "pkv_status_str", "pkv_indexing", "pkv_kv_store_rope",
                                          "pkv_paged_decode_attn_rope", "pkv_paged_decode_attn_valu",
                                          "pkv_prefill_plan", "pkv_paged_prefill_attn",
-                                         "pkv_paged_decode_attn_merged", "pkv_decode_step"])
+                                         "pkv_paged_decode_attn_merged", "pkv_decode_step",
+                                         "pkv_paged_decode_attn_merged_static"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -54,7 +55,7 @@ def test_contracted_split_count_signature():
 
 
 def test_status_strings(lib):
-    for code in [OK, NULL, SHAPE, UNSUP, ALIGN, -5, 7]:
+    for code in [OK, NULL, SHAPE, UNSUP, ALIGN, -5, SCRATCH, 7]:
         assert lib.pkv_status_str(code)
 
 
@@ -223,6 +224,32 @@ def test_merged_attention_validation(lib):
     assert _merged(lib, o=ctypes.c_void_p(260)) == ALIGN
     assert _merged(lib, S=1, o=None, lse=None, out=None) == NULL    # one split: only out is needed
     assert _merged(lib, S=1, o=None, lse=None, out=ctypes.c_void_p(264)) == ALIGN
+
+
+def _static(lib, out=ctypes.c_void_p(256), **kw):
+    p = ctypes.c_void_p(256)
+    a = dict(q=p, k=p, v=p, pt=p, sl=p, B=2, Hq=8, Hkv=2, D=128, P=16, pages=10, mp=4, L=64, S=2,
+             scale=0.088)
+    a.update(kw)
+    return lib.pkv_paged_decode_attn_merged_static(a["q"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["Hq"],
+                                                   a["Hkv"], a["D"], a["P"], a["pages"], a["mp"], a["L"],
+                                                   a["S"], a["scale"], out, None, None)
+
+
+def test_static_scratch_validation(lib):
+    """The no-allocation call checks its arguments like the merged call, and
+    rejects partials beyond its 16 MiB scratch before touching the GPU."""
+    assert _static(lib, B=0) == OK
+    assert _static(lib, q=None) == NULL
+    assert _static(lib, out=None) == NULL
+    assert _static(lib, out=ctypes.c_void_p(258)) == ALIGN
+    assert _static(lib, D=96) == UNSUP
+    assert _static(lib, S=0) == SHAPE
+    # B * Hq * S * (D + 1) floats against 4 Mi: 128 * 32 * 8 * 129 = 4.2 Mi does not fit
+    big = dict(B=128, Hq=32, Hkv=8, pages=100000, mp=512, L=8192)
+    assert _static(lib, S=8, **big) == SCRATCH
+    assert _static(lib, S=1024, B=64, Hq=64, Hkv=8, pages=100000, mp=512, L=8192) == SCRATCH
+    assert _static(lib, S=1025) == SHAPE
 
 
 def _step(lib, kn=ctypes.c_void_p(256), stride=256, slots=ctypes.c_void_p(256), out=ctypes.c_void_p(256), **kw):
