@@ -26,6 +26,13 @@
 //   K and V are read once, so their loads carry the non-temporal hint: on
 //   gfx950 this measured ~10% faster than default-policy loads of the same
 //   addresses (the lines are not kept in L2 / the memory-side cache).
+//   With pages of >= 16 tokens a tile is one page's run of 16 slots: each
+//   tile's loads go through one buffer descriptor per pool (scalar base at
+//   the tile's first slot, a range that ends at the split's last position)
+//   and constant per-lane offsets, so they need no vector address arithmetic,
+//   and the slots past the range read zeros without touching memory.  The
+//   ring's steady state runs whole passes of NBUF tiles; the remaining tiles,
+//   already loaded, are computed after it, so no dummy tile is ever computed.
 //   Workgroup order: kv head fastest, then sequence, then split.  With one
 //   split this keeps the kv heads of a sequence (which read the same pages)
 //   launched together; with several, every sequence's first split is
@@ -54,6 +61,17 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 // streaming (non-temporal) 16-byte load for K/V rows, which are read exactly once
 __device__ __forceinline__ u32x4 ld16_stream(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+// Buffer descriptors (V#): base, no stride, a byte range; lanes whose offset
+// falls outside the range read zeros and touch no memory.  Dword 3 of a gfx9
+// descriptor: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), short(0), bytes, kRsrcWord3);
+}
+// streaming 16-byte load through a descriptor (cache policy nt)
+__device__ __forceinline__ u32x4 ld16_buf_stream(__amdgpu_buffer_rsrc_t r, int voffset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 2);
 }
 __device__ __forceinline__ void unpack8v(const u32x4 &v, float f[8]) {
 #pragma unroll
@@ -187,21 +205,27 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   int L = p.seq_lens[b];
   L = min(max(L, 0), p.max_pages << log2P);
   const int t1 = min(t0 + p.chunk, L);
+  // fused store: head g of the new K / V row (8 dims per entry), for the tile
+  // that holds position L - 1
+  [[maybe_unused]] __shared__ u32x4 sm_new[2][D / 8];
   if constexpr (kFuse) {
     // The step's store, fused: the split holding position L - 1 (split 0 for
     // an empty sequence) copies head g of the new K/V row to its pool slot,
     // 16 bytes per lane (the store's contract: an index outside the pool is
     // not written).  The attention takes position L - 1 from the new row
-    // itself, so no ordering with these writes is needed.
+    // itself, kept in LDS (ordered before its use by the barrier that opens
+    // the first page-id segment), so no ordering with the pool writes is needed.
     const int sw = L > 0 ? min((L - 1) / p.chunk, p.num_splits - 1) : 0;
     constexpr int LPR = D / 8;
     if (s == sw && wave == 0 && lane < 2 * LPR) {
       const int64_t slot = p.slots[b];
+      const size_t c = size_t(g) * D + 8 * (lane % LPR);
+      const uint16_t *src = (lane < LPR ? p.k_new : p.v_new) + size_t(b) * p.new_stride + c;
+      const u32x4 row = ld16(src);
+      sm_new[lane / LPR][lane % LPR] = row;
       if (slot >= 0 && slot < p.num_slots) {
-        const size_t c = size_t(g) * D + 8 * (lane % LPR);
-        const uint16_t *src = (lane < LPR ? p.k_new : p.v_new) + size_t(b) * p.new_stride + c;
         uint16_t *dst = const_cast<uint16_t *>(lane < LPR ? p.k_pool : p.v_pool) + size_t(slot) * p.Hkv * D + c;
-        *reinterpret_cast<u32x4 *>(dst) = ld16(src);
+        *reinterpret_cast<u32x4 *>(dst) = row;
       }
     }
   }
@@ -258,12 +282,12 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   const uint16_t *vbase = p.v_pool + size_t(g) * D + 8 * (lane % LPV);
   const uint16_t *qrow = p.q + (size_t(b) * p.Hq + size_t(g) * G) * D + 8 * (lane % LPV);
   const int vt = lane / LPV;
-  // fused store: position L - 1 is read from the new rows
-  [[maybe_unused]] const uint16_t *knew = nullptr, *vnew = nullptr;
-  if constexpr (kFuse) {
-    knew = p.k_new + size_t(b) * p.new_stride + size_t(g) * D + 8 * (lane % LPV);
-    vnew = p.v_new + size_t(b) * p.new_stride + size_t(g) * D + 8 * (lane % LPV);
-  }
+  // with whole-page tiles: byte offset of this lane's 16 bytes within the tile
+  // for each load i (token slot TPV * i + vt, head g, dims 8 * (lane % LPV))
+  const int row_bytes = int(row_stride) * 2;
+  [[maybe_unused]] int voff[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i) voff[i] = (TPV * i + vt) * row_bytes + (g * D + 8 * (lane % LPV)) * 2;
 
   struct Regs { u32x4 k[KS]; u32x4 v[KS]; int pid; };
 
@@ -291,28 +315,29 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
     // HBM again (lines loaded with the non-temporal hint are not retained).
     auto load_kv = [&](int k, Regs &rg, bool real) {
       const int tb = tw0 + kTile * k;
-      const uint16_t *kb = real ? kbase : qrow;
-      const uint16_t *vb = real ? vbase : qrow;
-      const size_t rs = real ? row_stride : 0;
       if constexpr (kPageTile) {
-        const int raw = __builtin_amdgcn_readfirstlane(sm_pid[(min(tb, last) >> log2P) - pga]);
+        // A tile lies inside one page (tiles start on multiples of 16 within
+        // pages of >= 16 tokens): one descriptor per tile and pool, based at
+        // the tile's first slot and spanning its positions up to `last`.  The
+        // lanes of positions past `last` read zeros, as does every lane of a
+        // prefetch past the range (an empty span), and no load needs VALU
+        // address arithmetic.
+        const int raw = __builtin_amdgcn_readfirstlane(sm_pid[(tb >> log2P) - pga]);
         rg.pid = raw;
         const int pid = unsigned(raw) < unsigned(p.num_pages) ? raw : 0;
-        const size_t page_row = size_t(pid) << log2P;
+        const int64_t first_slot = (int64_t(pid) << log2P) + (tb & pmask);
+        const int span = real ? min(last - tb + 1, kTile) * row_bytes : 0;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_pool + first_slot * int64_t(row_stride), span);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_pool + first_slot * int64_t(row_stride), span);
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
-          const int tv = min(tb + TPV * i + vt, last);
-          const size_t row = page_row + (tv & pmask);
-          const uint16_t *ka = kb + row * rs, *va = vb + row * rs;
-          if constexpr (kFuse) {
-            const bool fresh = real && tv == L - 1;
-            ka = fresh ? knew : ka;
-            va = fresh ? vnew : va;
-          }
-          rg.k[i] = ld16_stream(ka);
-          rg.v[i] = ld16_stream(va);
+          rg.k[i] = ld16_buf_stream(rk, voff[i]);
+          rg.v[i] = ld16_buf_stream(rv, voff[i]);
         }
       } else {
+        const uint16_t *kb = real ? kbase : qrow;
+        const uint16_t *vb = real ? vbase : qrow;
+        const size_t rs = real ? row_stride : 0;
         rg.pid = sm_pid[(min(tb + (lane & 15), last) >> log2P) - pga];   // page of this lane's score token
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
@@ -320,20 +345,27 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
           const int rv = sm_pid[(tv >> log2P) - pga];
           const int pv = unsigned(rv) < unsigned(p.num_pages) ? rv : 0;
           const size_t row = (size_t(pv) << log2P) + (tv & pmask);
-          const uint16_t *ka = kb + row * rs, *va = vb + row * rs;
-          if constexpr (kFuse) {
-            const bool fresh = real && tv == L - 1;
-            ka = fresh ? knew : ka;
-            va = fresh ? vnew : va;
-          }
-          rg.k[i] = ld16_stream(ka);
-          rg.v[i] = ld16_stream(va);
+          rg.k[i] = ld16_stream(kb + row * rs);
+          rg.v[i] = ld16_stream(vb + row * rs);
         }
       }
     };
 
-    auto compute = [&](int k, const Regs &rg, bool active) {
+    auto compute = [&](int k, Regs rg) {
       const int tb = tw0 + kTile * k;
+      if constexpr (kFuse) {
+        // the one tile that holds position L - 1 (a wave-uniform test): the
+        // lanes that loaded that position's pool slot take the new row instead
+        if (L - 1 >= tb && L - 1 < tb + kTile) {
+          const u32x4 kn = sm_new[0][lane % LPV], vn = sm_new[1][lane % LPV];
+#pragma unroll
+          for (int i = 0; i < KS; ++i) {
+            const bool fresh = min(tb + TPV * i + vt, last) == L - 1;
+            rg.k[i] = fresh ? kn : rg.k[i];
+            rg.v[i] = fresh ? vn : rg.v[i];
+          }
+        }
+      }
       // re-lay K from whole rows into the B operand (lane = token, 8 dims per k-step)
       unsigned char *kt = sm_k[wave];
       wave_lds_sync();
@@ -348,7 +380,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j], as_bf16x8(kb), c, 0, 0, 0);
       }
       // this lane: token tb + (lane & 15), heads 4 * (lane >> 4) + r
-      const bool valid = active && tb + (lane & 15) <= last;
+      const bool valid = tb + (lane & 15) <= last;
       const bool bad = unsigned(rg.pid) >= unsigned(p.num_pages);
       float alpha[4], pr[4];
 #pragma unroll
@@ -400,9 +432,10 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
     };
 
     // Ring of NBUF register tiles: NBUF-1 tiles are in flight while one is
-    // computed.  The body is branch-free: loads past the range read a q row
-    // and their compute is fully masked, so the compiler can neither sink a
-    // prefetch next to its use nor merge waits across paths.
+    // computed.  The steady-state body is branch-free: loads past the range
+    // read a q row (an L2 hit) and are never computed, so the compiler can
+    // neither sink a prefetch next to its use nor merge waits across paths.
+    // The last my_tiles % NBUF tiles, already loaded, are computed after it.
     if (my_tiles > 0) {
       const int lt = my_tiles - 1;
       Regs rg[NBUF];
@@ -411,14 +444,18 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
         load_kv(min(j, lt), rg[j], j <= lt);
         pin_issue_order();
       }
-      for (int k = 0; k < my_tiles; k += NBUF) {
+      int k = 0;
+      for (; k + NBUF <= my_tiles; k += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
           load_kv(min(k + u + NBUF - 1, lt), rg[(u + NBUF - 1) % NBUF], k + u + NBUF - 1 <= lt);
           pin_issue_order();
-          compute(k + u, rg[u], k + u < my_tiles);
+          compute(k + u, rg[u]);
         }
       }
+#pragma unroll
+      for (int u = 0; u < NBUF - 1; ++u)
+        if (k + u < my_tiles) compute(k + u, rg[u]);
     }
     sa = sb;
   }

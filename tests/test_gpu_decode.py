@@ -271,11 +271,14 @@ def test_errors_raise(gpu_device, decode_kernel):
                               kernel=decode_kernel)
 
 
-def test_nan_query_gives_nan_rows(gpu_device, decode_kernel):
-    """Every score of a row NaN: the row is NaN (as in the oracle), not an empty split's zeros."""
+@pytest.mark.parametrize("head", [2, 0])
+def test_nan_query_gives_nan_rows(gpu_device, decode_kernel, head):
+    """Every score of a row NaN: the row is NaN (as in the oracle), not an empty
+    split's zeros, and no other row of its kv-head group (head 0 is the row the
+    matrix-core kernel's prefetches past a wave's range read) is touched."""
     inp = inputs("tiny_gqa")
     q = inp.q.copy()
-    q[1, 2] = W.BF16_NAN
+    q[1, head] = W.BF16_NAN
     st = DeviceStep(inp, gpu_device, kernel=decode_kernel)
     st.q = bf16_dev(q, gpu_device)
     (out, lse), _, _ = st.step(splits=3, want_lse=True)
@@ -283,8 +286,8 @@ def test_nan_query_gives_nan_rows(gpu_device, decode_kernel):
     kf, vf = inp.pools_after_store()
     ref, ref_lse = oracle.paged_decode(q, kf, vf, inp.page_table, inp.seq_lens)
     g = host_f64_from_bf16(out)
-    assert np.isnan(ref[1, 2]).all() and np.isnan(ref_lse[1, 2])
-    assert np.isnan(g[1, 2]).all() and torch.isnan(lse[1, 2])
+    assert np.isnan(ref[1, head]).all() and np.isnan(ref_lse[1, head])
+    assert np.isnan(g[1, head]).all() and torch.isnan(lse[1, head])
     mask = np.ones(g.shape[:2], bool)
-    mask[1, 2] = False
+    mask[1, head] = False
     assert np.isfinite(g[mask]).all()
