@@ -45,6 +45,29 @@ SIGNATURES = [
 
 _lib = None
 
+BENCH_LIB_PATH = Path(__file__).resolve().parent / "libpkv_bench.so"
+# include/pkv_bench.h: the copy kernels that bound the store (measurement only)
+BENCH_SIGNATURES = [
+    ("pkvb_copy_linear", _i32, [_p, _p, _i64, _p]),
+    ("pkvb_copy_page_runs", _i32, [_p, _p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _i64, _p]),
+]
+_bench_lib = None
+
+
+def bench_lib() -> ctypes.CDLL:
+    """libpkv_bench.so (bench.py's copy ceilings); raises if it is not built."""
+    global _bench_lib
+    if _bench_lib is None:
+        if not BENCH_LIB_PATH.exists():
+            raise RuntimeError(f"{BENCH_LIB_PATH} is not built; run `python -m paged_kv_gqa_store_amd.build`")
+        handle = ctypes.CDLL(str(BENCH_LIB_PATH))
+        for name, res, args in BENCH_SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _bench_lib = handle
+    return _bench_lib
+
 
 def lib() -> ctypes.CDLL:
     global _lib

@@ -19,6 +19,9 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libpkv.so"
 SOURCES = ["pkv_api.hip", "pkv_store.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_prefill.hip"]
+# copy kernels that bound the store (bench.py's ceilings), a library of their own
+BENCH_LIB = PKG / "libpkv_bench.so"
+BENCH_SOURCES = ["pkv_bench.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -54,11 +57,17 @@ def _run(procs, verbose):
 
 
 def build(verbose: bool = False) -> Path:
-    """Compile every source to an object (in parallel), then link libpkv.so."""
-    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
+    """Compile every source to an object (in parallel), then link libpkv.so
+    and libpkv_bench.so."""
+    _build_lib(BENCH_LIB, BENCH_SOURCES, verbose)
+    return _build_lib(LIB, SOURCES, verbose)
+
+
+def _build_lib(lib: Path, sources, verbose: bool) -> Path:
+    tmp = lib.with_suffix(f".so.tmp{os.getpid()}")
     with tempfile.TemporaryDirectory(prefix="pkv_build_") as objdir:
         objs, procs = [], []
-        for src in SOURCES:
+        for src in sources:
             obj = str(Path(objdir) / (Path(src).stem + ".o"))
             cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", str(CSRC / src), "-o", obj]
             if verbose:
@@ -70,8 +79,8 @@ def build(verbose: bool = False) -> Path:
         if verbose:
             print(" ".join(cmd), flush=True)
         _run([(cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

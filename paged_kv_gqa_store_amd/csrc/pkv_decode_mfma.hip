@@ -170,9 +170,11 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
     b = (blockIdx.x / p.Hkv) % p.B;
     s = blockIdx.x / (p.Hkv * p.B);
   }
-  if (!kFuse && empty_pair) {
+  if (empty_pair && (!kFuse || s > 0)) {
     // the result of an empty split (as in the epilogue), without its loads:
-    // in a ragged batch these pairs are many, and they run last
+    // in a ragged batch these pairs are many, and they run last.  (A later
+    // split never holds position L - 1; split 0 of an empty sequence takes the
+    // full path, which stores the step's row as the unfused step would.)
     for (int idx = threadIdx.x; idx < G * D; idx += kWaves * 64) {
       const int h = idx / D, d = idx % D;
       const size_t frow = size_t(b) * p.Hq + size_t(g) * G + h;

@@ -256,6 +256,25 @@ def bulk_fill_rows(inp: Inputs, seed: int | None = None):
     return k_rows, v_rows, slots
 
 
+def bulk_fill_runs(inp: Inputs):
+    """The bulk fill of :func:`bulk_fill_rows` as runs of consecutive rows that
+    land in consecutive slots (one run per page a sequence fills): int32
+    arrays (first source row, first destination slot, rows) per run."""
+    cfg = inp.cfg
+    src, dst, rows = [], [], []
+    r = 0
+    for b in range(cfg.B):
+        L = int(inp.seq_lens[b])
+        for j in range(-(-L // cfg.P)):
+            n = min(cfg.P, L - j * cfg.P)
+            src.append(r)
+            dst.append(int(inp.page_table[b, j]) * cfg.P)
+            rows.append(n)
+            r += n
+    as32 = lambda a: np.asarray(a, np.int64).astype(np.int32)
+    return as32(src), as32(dst), as32(rows)
+
+
 @dataclass(frozen=True)
 class PrefillConfig:
     """A paged prefill batch: request b has kv_lens[b] tokens in the pool, the
@@ -415,7 +434,7 @@ def sample_rows(cfg: Config, k: int, seed: int = 7) -> np.ndarray:
 
 
 __all__ = ["Config", "WORKLOADS", "Inputs", "make_inputs", "custom_config", "contiguous_layout",
-           "bulk_fill_rows", "kv_bytes", "attention_bytes", "store_bytes", "roofline_us",
+           "bulk_fill_rows", "bulk_fill_runs", "kv_bytes", "attention_bytes", "store_bytes", "roofline_us",
            "to_bf16_bits", "bf16_bits_to_f32", "sample_rows", "IndexingConfig", "INDEXING",
            "make_indexing_inputs", "indexing_bytes", "rope_tables", "PrefillConfig", "PREFILL",
            "make_prefill_inputs", "prefill_flops"]

@@ -54,6 +54,23 @@ def test_contracted_split_count_signature():
     assert names == ["B", "Hq", "Hkv", "max_seq_len", "total_tokens", "page_size", "num_cus"]
 
 
+def test_bench_library_exports_its_header():
+    text = (ROOT / "include" / "pkv_bench.h").read_text()
+    names = sorted(set(re.findall(r"^\S.*?\b(pkvb_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+    assert names == ["pkvb_copy_linear", "pkvb_copy_page_runs"]
+    blib = _lib.bench_lib()
+    assert {s[0] for s in _lib.BENCH_SIGNATURES} == set(names)
+    p = ctypes.c_void_p(256)
+    # argument checks return before any launch
+    assert blib.pkvb_copy_linear(p, p, 0, None) == OK
+    assert blib.pkvb_copy_linear(p, p, 24, None) == SHAPE
+    assert blib.pkvb_copy_linear(None, p, 32, None) == NULL
+    assert blib.pkvb_copy_linear(ctypes.c_void_p(264), p, 32, None) == ALIGN
+    assert blib.pkvb_copy_page_runs(p, p, 10, p, p, 10, p, p, p, 0, 2048, None) == OK
+    assert blib.pkvb_copy_page_runs(p, p, 10, p, p, 10, p, p, p, 3, 2047, None) == SHAPE
+    assert blib.pkvb_copy_page_runs(p, p, 10, p, p, 10, None, p, p, 3, 2048, None) == NULL
+
+
 def test_status_strings(lib):
     for code in [OK, NULL, SHAPE, UNSUP, ALIGN, -5, SCRATCH, 7]:
         assert lib.pkv_status_str(code)
