@@ -370,11 +370,12 @@ pkv_status pkv_decode_step(const void *q, const void *k_new, const void *v_new,
  * batches underfill the GPU despite split-KV (AstrAI "CUDA Kernels", sections
  * "File Layout" and "Known Optimization Targets"); the rule is a reading,
  * tuned by measurement on MI355X.  This form knows neither the group size nor
- * the lengths, so it takes the cautious side of pkv_num_splits_batch: one q
- * head per kv head and a ragged batch,
- *     pkv_num_splits(B, Hkv, L, P, cus) == pkv_num_splits_batch(B, Hkv, Hkv, L, -1, P, cus)
- *     = clamp(max(ceil(num_cus / (B * Hkv)), ceil(max_seq_len / 2048)),
- *             1, min(1024, max(1, ceil(max_seq_len / 256))))
+ * the lengths, so it counts one workgroup per (sequence, kv head, split) and
+ * takes the batch as ragged:
+ *     S = clamp(max(ceil(num_cus / (B * Hkv)), ceil(max_seq_len / 2048)),
+ *               1, min(1024, max(1, ceil(max_seq_len / 256))))
+ * pkv_num_splits_batch is the form for callers that know the group size and
+ * the token count.
  * Returns >= 1 for valid arguments, PKV_ERR_SHAPE otherwise (B, Hkv or num_cus
  * below 1, max_seq_len negative, page_size not a power of two).
  */
@@ -384,13 +385,16 @@ int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page
 /*
  * pkv_num_splits_batch -- pkv_num_splits for a batch whose group size and
  * token count the caller knows (a serving scheduler does); host only.
- *     streams = B * Hkv                         one workgroup each per split
+ *     streams = B * Hkv / hb                    workgroups per split: hb = 1, or
+ *               with one q head per kv head (Hq == Hkv) the row kernel's heads
+ *               per workgroup, counted as 8 when Hkv % 8 == 0, else 4 when
+ *               Hkv % 4 == 0 (512 / D is 8 at D = 64 and 4 at D = 128)
  *     S_fill  = ceil(w * num_cus / streams)     w = 2 if Hq/Hkv >= 8, else 1
  *     ragged  = total_tokens < 0 (unknown) or total_tokens < 0.9 * B * max_seq_len
  *     S       = ragged ? max(S_fill, ceil(max_seq_len / 2048)) : S_fill
  *     S       = clamp(S, 1, min(1024, max(1, ceil(max_seq_len / 256))))
  * total_tokens is the sum of the batch's sequence lengths, or any negative
- * value when unknown.  Uniform batches keep one split per (sequence, kv head)
+ * value when unknown.  Uniform batches keep one split per workgroup stream
  * while that fills the GPU; ragged ones are cut into splits of at most 2048
  * positions, so that the workgroups of long sequences are not the last to
  * finish.  Returns as pkv_num_splits (also PKV_ERR_SHAPE when Hq is not a

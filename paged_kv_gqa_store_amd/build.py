@@ -18,7 +18,8 @@ PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libpkv.so"
-SOURCES = ["pkv_api.hip", "pkv_store.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_prefill.hip"]
+SOURCES = ["pkv_api.hip", "pkv_store.hip", "pkv_decode.hip", "pkv_decode_mfma.hip", "pkv_decode_rows.hip",
+           "pkv_prefill.hip"]
 # copy kernels that bound the store (bench.py's ceilings), a library of their own
 BENCH_LIB = PKG / "libpkv_bench.so"
 BENCH_SOURCES = ["pkv_bench.hip"]

@@ -133,9 +133,9 @@ pkv_status launch_merged(pkv::DecodeParams &p, void *out, float *lse_out, hipStr
     p.lse_out = lse_out;
     p.o_partial = nullptr;
     p.lse_partial = nullptr;
-    return pkv::launch_paged_decode_mfma(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    return pkv::launch_paged_decode(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
   }
-  if (pkv::launch_paged_decode_mfma(p, s) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_paged_decode(p, s) != hipSuccess) return PKV_ERR_HIP;
   const hipError_t e = pkv::launch_decode_merge(p.o_partial, p.lse_partial, p.B * p.Hq, p.D,
                                                 p.num_splits, static_cast<uint16_t *>(out),
                                                 lse_out, s);
@@ -199,7 +199,12 @@ int32_t pkv_num_splits_batch(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq
   if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || max_seq_len < 0 || !is_pow2(page_size) ||
       num_cus < 1)
     return PKV_ERR_SHAPE;
-  const int64_t streams = int64_t(B) * Hkv;          // (sequence, kv head) pairs
+  // workgroups per split: one per (sequence, kv head), or with one q head per
+  // kv head one per (sequence, block of 512 / D kv heads): 8 heads at D = 64,
+  // 4 at D = 128 (D is not an argument: counted as 8, which errs towards more
+  // splits)
+  const int64_t hb = Hq == Hkv ? (Hkv % 8 == 0 ? 8 : (Hkv % 4 == 0 ? 4 : 1)) : 1;
+  const int64_t streams = int64_t(B) * Hkv / hb;
   const int64_t wg_per_cu = Hq / Hkv >= 8 ? 2 : 1;   // workgroups that keep one CU busy
   int64_t s = ceil_div(wg_per_cu * num_cus, streams);
   const bool uniform = total_tokens >= 0 && total_tokens * 10 >= int64_t(B) * max_seq_len * 9;
@@ -216,8 +221,17 @@ int32_t pkv_num_splits_batch(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_seq
 
 int32_t pkv_num_splits(int32_t B, int32_t Hkv, int32_t max_seq_len, int32_t page_size,
                        int32_t num_cus) {
-  // group size and token count unknown: one q head per kv head, lengths ragged
-  return pkv_num_splits_batch(B, Hkv, Hkv, max_seq_len, -1, page_size, num_cus);
+  // group size and token count unknown: one workgroup per (sequence, kv head)
+  // and split, lengths ragged
+  if (B < 1 || Hkv < 1 || max_seq_len < 0 || !is_pow2(page_size) || num_cus < 1) return PKV_ERR_SHAPE;
+  int64_t s = ceil_div(num_cus, int64_t(B) * Hkv);
+  const int64_t s_bal = ceil_div(max_seq_len, 2048);
+  if (s_bal > s) s = s_bal;
+  int64_t cap = ceil_div(max_seq_len, 256);
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return int32_t(s < 1 ? 1 : s);
 }
 
 pkv_status pkv_kv_store(void *k_pool, void *v_pool, int64_t num_slots, int64_t pool_row_stride,
@@ -297,7 +311,7 @@ pkv_status pkv_paged_decode_attn(const void *q, const void *k_pool, const void *
                                          page_size, num_pages, max_pages_per_seq, max_seq_len,
                                          num_splits, scale, o_partial, lse_partial, p);
   if (st != PKV_OK || p.B == 0) return st;
-  hipError_t e = pkv::launch_paged_decode_mfma(p, static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -340,7 +354,7 @@ pkv_status pkv_paged_decode_attn_rope(const void *q, const void *k_pool, const v
   p.rope_cos = rope_cos;
   p.rope_sin = rope_sin;
   p.rope_rows = rope_rows;
-  hipError_t e = pkv::launch_paged_decode_mfma(p, static_cast<hipStream_t>(stream));
+  hipError_t e = pkv::launch_paged_decode(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -479,9 +493,9 @@ pkv_status pkv_decode_step(const void *q, const void *k_new, const void *v_new,
   if (one) {
     p.out = static_cast<uint16_t *>(out);
     p.lse_out = lse_out;
-    return pkv::launch_paged_decode_mfma(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    return pkv::launch_paged_decode(p, s) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
   }
-  if (pkv::launch_paged_decode_mfma(p, s) != hipSuccess) return PKV_ERR_HIP;
+  if (pkv::launch_paged_decode(p, s) != hipSuccess) return PKV_ERR_HIP;
   const hipError_t e = pkv::launch_decode_merge(o_partial, lse_partial, B * Hq, D, num_splits,
                                                 static_cast<uint16_t *>(out), lse_out, s);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;

@@ -554,6 +554,11 @@ hipError_t launch_mfma(const DecodeParams &p, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream) {
+  if (paged_decode_rows_applies(p)) return launch_paged_decode_rows(p, stream);
+  return launch_paged_decode_mfma(p, stream);
+}
+
 hipError_t launch_paged_decode_mfma(const DecodeParams &p, hipStream_t stream) {
 #define PKV_CASE(DD, GG)                                                        \
   if (p.D == DD && p.G == GG)                                                   \

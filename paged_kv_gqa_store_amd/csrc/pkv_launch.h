@@ -54,11 +54,18 @@ hipError_t launch_gather_rows(void *out, const void *weight, int64_t length, con
                               int64_t n, int64_t start, int64_t row_b, int unit_b,
                               hipStream_t stream);
 
-// Split-KV decode: the matrix-core kernel (every decode entry point) and the
-// all-VALU kernel (only pkv_paged_decode_attn_valu, the measured alternative
-// of that design choice; both honour the same contract).
+// Split-KV decode: the matrix-core kernel, the row kernel for one q head per
+// kv head, and the all-VALU kernel (only pkv_paged_decode_attn_valu, the
+// measured alternative of the matrix-core choice); all honour the same contract.
 hipError_t launch_paged_decode_valu(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_paged_decode_mfma(const DecodeParams &p, hipStream_t stream);
+// One q head per kv head: the kernel that reads whole token rows (512 / D heads
+// per workgroup), when Hkv is a multiple of 512 / D.
+bool paged_decode_rows_applies(const DecodeParams &p);
+hipError_t launch_paged_decode_rows(const DecodeParams &p, hipStream_t stream);
+// The decode attention behind every decode entry point: the row kernel where
+// it applies, the matrix-core kernel otherwise.
+hipError_t launch_paged_decode(const DecodeParams &p, hipStream_t stream);
 
 hipError_t launch_decode_merge(const float *o_partial, const float *lse_partial, int rows, int D,
                                int num_splits, uint16_t *out, float *lse_out, hipStream_t stream);

@@ -90,16 +90,26 @@ def test_split_heuristic_on_the_five_workloads(lib):
     assert lib.pkv_num_splits_batch(4, 64, 8, 65536, -1, 16, 256) == 32
 
 
-def test_contracted_split_count_is_the_cautious_batch_form(lib):
-    """Without Hq and the token count: one q head per kv head, ragged lengths."""
+def test_contracted_split_count_formula(lib):
+    """Without Hq and the token count: one workgroup per (sequence, kv head,
+    split), ragged lengths."""
     for B in [1, 2, 4, 32, 64, 128, 500]:
         for Hkv in [1, 8, 16]:
             for L in [0, 1, 100, 255, 256, 2049, 4096, 8192, 65536, 100000]:
                 for P in [1, 16]:
                     s = lib.pkv_num_splits(B, Hkv, L, P, 256)
-                    assert s == lib.pkv_num_splits_batch(B, Hkv, Hkv, L, -1, P, 256)
                     cap = min(1024, max(1, -(-L // 256)))
                     assert s == max(1, min(cap, max(-(-256 // (B * Hkv)), -(-L // 2048))))
+                    if Hkv == 1:   # G = 1 with one kv head: no head blocks, the batch form agrees
+                        assert s == lib.pkv_num_splits_batch(B, Hkv, Hkv, L, -1, P, 256)
+
+
+def test_batch_split_count_counts_head_blocks_for_one_q_head_per_kv_head(lib):
+    # 16 sequences x 16 kv heads, one q head each: 32 row-kernel workgroups per split
+    assert lib.pkv_num_splits_batch(16, 16, 16, 4096, 16 * 4096, 1, 256) == 8
+    # the same heads in groups of 4 q heads: 256 workgroups per split
+    assert lib.pkv_num_splits_batch(16, 64, 16, 4096, 16 * 4096, 1, 256) == 1
+    assert lib.pkv_num_splits_batch(16, 12, 12, 4096, 16 * 4096, 1, 256) == 6   # 12 % 8: blocks of 4
     assert lib.pkv_num_splits(32, 8, 4096, 16, 256) == 2
     assert lib.pkv_num_splits(0, 8, 10, 16, 256) == SHAPE
     assert lib.pkv_num_splits(1, 0, 10, 16, 256) == SHAPE
