@@ -181,7 +181,16 @@ hipError_t launch_valu(const DecodeParams &p, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one wave per (b, h) row, D/64 dims per lane, splits in ascending order.
+// Merge: one wave per (b, h) row, D/64 dims per lane.  Lane s reads split s's
+// lse (64 splits per pass), the wave takes their max; then each split's
+// weight is broadcast from its lane and the splits are accumulated in
+// ascending order (the fixed order of the fp32 sums), with the o loads of
+// several splits in flight.
+__device__ __forceinline__ float wave_max(float x) {
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restrict__ o_part,
                                                            const float *__restrict__ lse_part,
@@ -195,21 +204,43 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restri
   const float *lp = lse_part + size_t(row) * S;
   float M = -INFINITY;
   bool nan = false;
-  for (int s = 0; s < S; ++s) {
-    const float x = lp[s];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const float x = s0 + lane < S ? lp[s0 + lane] : -INFINITY;
     nan |= (x != x);
     M = (x > M) ? x : M;
   }
+  M = wave_max(M);
+  nan = __any(nan);
   float num[DPL], den = 0.f;
 #pragma unroll
   for (int j = 0; j < DPL; ++j) num[j] = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float w = fast_exp2((lp[s] - M) * kLog2e);
-      den += w;
-      const float *os = o_part + (size_t(row) * S + s) * D + lane * DPL;
+    const float *orow = o_part + size_t(row) * S * D + lane * DPL;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+      const float x = s0 + lane < S ? lp[s0 + lane] : -INFINITY;
+      const float wl = fast_exp2((x - M) * kLog2e);
+      const int n = min(64, S - s0);
+      int i = 0;
+      for (; i + 8 <= n; i += 8) {   // eight splits' loads in flight, then their sums in order
+        float ov[8][DPL];
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) num[j] = fmaf(w, os[j], num[j]);
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) ov[u][j] = orow[size_t(s0 + i + u) * D + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i + u));
+          den += w;
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) num[j] = fmaf(w, ov[u][j], num[j]);
+        }
+      }
+      for (; i < n; ++i) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+        den += w;
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) num[j] = fmaf(w, orow[size_t(s0 + i) * D + j], num[j]);
+      }
     }
   }
   uint32_t bits[DPL];
