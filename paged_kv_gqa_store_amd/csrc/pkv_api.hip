@@ -82,7 +82,7 @@ pkv_status attention_params(const void *q, const void *k_pool, const void *v_poo
   p.chunk = max_seq_len == 0 ? page_size : pkv_split_chunk(max_seq_len, num_splits, page_size);
   // few (sequence, split) pairs and several splits: the kernel ranks the pairs
   // by length (one per thread of a workgroup) and runs them longest first
-  p.longest_first = num_splits > 1 && int64_t(B) * num_splits <= 256;
+  p.longest_first = num_splits > 1 && int64_t(B) * num_splits <= 256 && p.chunk < (1 << 22);
   p.scale_log2 = scale * 1.4426950408889634f;
   return PKV_OK;
 }

@@ -141,31 +141,13 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   int g = blockIdx.x % p.Hkv, b, s;
   bool empty_pair = false;        // a split past its sequence's end (known in the longest-first order)
   if (p.longest_first) {
-    __shared__ int sm_len[kWaves * 64];
+    __shared__ __attribute__((aligned(16))) unsigned sm_key[kWaves * 64];
     __shared__ int sm_pick;
-    const int n = p.B * p.num_splits;   // <= kWaves * 64 (checked on the host)
-    const int i = threadIdx.x;
-    if (i < n) {
-      const int Li = min(max(p.seq_lens[i % p.B], 0), p.max_pages << p.page_log2);
-      sm_len[i] = max(0, min(p.chunk, Li - (i / p.B) * p.chunk));
-    }
-    __syncthreads();
-    // rank = pairs longer than this one, or as long with a lower index: a
-    // permutation of 0 .. n-1, so exactly one thread matches
-    const int target = blockIdx.x / p.Hkv;
-    if (i < n) {
-      const int li = sm_len[i];
-      int r = 0;
-      for (int j = 0; j < n; ++j) {
-        const int lj = sm_len[j];
-        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
-      }
-      if (r == target) sm_pick = i;
-    }
-    __syncthreads();
-    b = sm_pick % p.B;
-    s = sm_pick / p.B;
-    empty_pair = sm_len[sm_pick] == 0;
+    const int2 pk = pick_longest_first(p.seq_lens, p.B, p.num_splits, p.chunk, p.max_pages << p.page_log2,
+                                       blockIdx.x / p.Hkv, sm_key, &sm_pick);
+    b = pk.x % p.B;
+    s = pk.x / p.B;
+    empty_pair = pk.y == 0;
   } else {
     b = (blockIdx.x / p.Hkv) % p.B;
     s = blockIdx.x / (p.Hkv * p.B);

@@ -81,29 +81,13 @@ __global__ __launch_bounds__(256) void paged_decode_rows_kernel(DecodeParams p) 
   int b, s;
   bool empty_pair = false;
   if (p.longest_first) {
-    __shared__ int sm_len[kWaves * 64];
+    __shared__ __attribute__((aligned(16))) unsigned sm_key[kWaves * 64];
     __shared__ int sm_pick;
-    const int n = p.B * p.num_splits;   // <= 256 (checked on the host)
-    const int i = threadIdx.x;
-    if (i < n) {
-      const int Li = min(max(p.seq_lens[i % p.B], 0), p.max_pages << p.page_log2);
-      sm_len[i] = max(0, min(p.chunk, Li - (i / p.B) * p.chunk));
-    }
-    __syncthreads();
-    const int target = blockIdx.x / nhb;
-    if (i < n) {
-      const int li = sm_len[i];
-      int r = 0;
-      for (int j = 0; j < n; ++j) {
-        const int lj = sm_len[j];
-        r += (lj > li || (lj == li && j < i)) ? 1 : 0;
-      }
-      if (r == target) sm_pick = i;
-    }
-    __syncthreads();
-    b = sm_pick % p.B;
-    s = sm_pick / p.B;
-    empty_pair = sm_len[sm_pick] == 0;
+    const int2 pk = pick_longest_first(p.seq_lens, p.B, p.num_splits, p.chunk, p.max_pages << p.page_log2,
+                                       blockIdx.x / nhb, sm_key, &sm_pick);
+    b = pk.x % p.B;
+    s = pk.x / p.B;
+    empty_pair = pk.y == 0;
   } else {
     b = (blockIdx.x / nhb) % p.B;
     s = blockIdx.x / (nhb * p.B);
