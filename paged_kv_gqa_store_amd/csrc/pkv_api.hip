@@ -33,6 +33,11 @@ int copy_unit(std::initializer_list<uint64_t> vals) {
 }
 
 constexpr int kMaxSplits = 1024;
+// (sequence, split) pairs the decode kernels rank longest first.  Every
+// workgroup ranks all of them (n^2 / 256 key comparisons per thread): at 512
+// pairs (the ragged batch at 8 splits) that cost more than the finer split
+// saved (251 against 194 us), at 1024 it took the launch to 856 us.
+constexpr int64_t kMaxRankedPairs = 256;
 
 
 // Validates the arguments shared by both attention entry points and fills the
@@ -82,7 +87,7 @@ pkv_status attention_params(const void *q, const void *k_pool, const void *v_poo
   p.chunk = max_seq_len == 0 ? page_size : pkv_split_chunk(max_seq_len, num_splits, page_size);
   // few (sequence, split) pairs and several splits: the kernel ranks the pairs
   // by length (one per thread of a workgroup) and runs them longest first
-  p.longest_first = num_splits > 1 && int64_t(B) * num_splits <= 256 && p.chunk < (1 << 22);
+  p.longest_first = num_splits > 1 && int64_t(B) * num_splits <= kMaxRankedPairs && p.chunk < (1 << 21);
   p.scale_log2 = scale * 1.4426950408889634f;
   return PKV_OK;
 }

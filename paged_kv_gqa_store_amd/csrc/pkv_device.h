@@ -44,37 +44,48 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Longest-first order of the (sequence, split) pairs of a decode launch: the
 // workgroups of pair rank r (r-th longest; equal lengths in index order) come
-// r-th in the grid.  Every workgroup ranks all n <= blockDim.x pairs (one per
-// thread) in LDS and returns the pair whose rank is `target` (pair index
-// i = b + B * s) and its length.  Key of pair i: length * 512 + (511 - i)
-// (unique, ordered as length then lower index; lengths < 2^22, checked on the
-// host), compared four at a time; padding keys are 0, below every pair's.
-// sm_key: at least blockDim.x rounded up to 4 ints, 16-byte aligned.
+// r-th in the grid.  Every workgroup ranks all n <= 4 * blockDim.x pairs
+// (thread i the pairs i, i + blockDim.x, ...) in LDS and returns the pair
+// whose rank is `target` (pair index i = b + B * s) and its length.  Key of
+// pair i: length * 2048 + (2047 - i) (unique, ordered as length then lower
+// index; lengths < 2^21, checked on the host), compared four at a time;
+// padding keys are 0, below every pair's.
+// sm_key: 4 * blockDim.x unsigned, 16-byte aligned.
 __device__ __forceinline__ int2 pick_longest_first(const int32_t *seq_lens, int B, int num_splits,
                                                    int chunk, int max_len, int target,
                                                    unsigned *sm_key, int *sm_pick) {
   const int n = B * num_splits;
-  const int i = threadIdx.x;
-  unsigned key = 0u;
-  if (i < n) {
-    const int Li = min(max(seq_lens[i % B], 0), max_len);
-    const int len = max(0, min(chunk, Li - (i / B) * chunk));
-    key = unsigned(len) * 512u + unsigned(511 - i);
-  }
-  sm_key[i] = key;
-  __syncthreads();
-  if (i < n) {
-    int r = 0;
-    const uint4 *k4 = reinterpret_cast<const uint4 *>(sm_key);
-    for (int j = 0; j < (n + 3) / 4; ++j) {
-      const uint4 k = k4[j];
-      r += (k.x > key) + (k.y > key) + (k.z > key) + (k.w > key);
+  const int nt = blockDim.x;
+  unsigned key[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = threadIdx.x + u * nt;
+    key[u] = 0u;
+    if (i < n) {
+      const int Li = min(max(seq_lens[i % B], 0), max_len);
+      const int len = max(0, min(chunk, Li - (i / B) * chunk));
+      key[u] = unsigned(len) * 2048u + unsigned(2047 - i);
     }
-    if (r == target) *sm_pick = i;
+    sm_key[i] = key[u];
+  }
+  __syncthreads();
+  const int nq = (n + 3) / 4;
+  const uint4 *k4 = reinterpret_cast<const uint4 *>(sm_key);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = threadIdx.x + u * nt;
+    if (i < n) {
+      int r = 0;
+      for (int j = 0; j < nq; ++j) {
+        const uint4 k = k4[j];
+        r += (k.x > key[u]) + (k.y > key[u]) + (k.z > key[u]) + (k.w > key[u]);
+      }
+      if (r == target) *sm_pick = i;
+    }
   }
   __syncthreads();
   const int pick = *sm_pick;
-  return make_int2(pick, int(sm_key[pick] >> 9));
+  return make_int2(pick, int(sm_key[pick] >> 11));
 }
 
 }  // namespace pkv
