@@ -79,16 +79,25 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 16-byte chunk permutation of K/V row r (only r & 15 matters): an XOR with a
-// bit shuffle of r such that chunk c of 16 consecutive rows lands on distinct
-// chunks, and so do chunks {2i, 2i + 1} of rows 4a .. 4a + 3 (D = 128: 16
-// chunks per 256-byte row; D = 64: 8 chunks per 128-byte row, where rows of
-// one parity also share banks).
+// 16-byte chunk permutation of K/V row r (only r & 15 matters), a bit
+// shuffle of r XORed into the chunk index.  The LDS serves 256 bytes a cycle
+// over 64 four-byte banks: 16 lanes of a 16-byte read, 32 lanes of an 8-byte
+// (transpose) read.  The shuffle makes each of them touch every bank once:
+//   - K reads, 16 rows at one logical chunk: the rows land on 16 distinct
+//     chunks (D = 128, 256-byte rows), or on distinct (row parity, chunk)
+//     pairs (D = 64, two 128-byte rows per bank line);
+//   - transpose reads of the 32-row kernel, 4 rows (4a .. 4a + 3) x a block of
+//     4 chunks: bits 2-3 of the shuffle (D = 128), or bit 2 across rows of
+//     one parity (D = 64), take distinct values on those rows, so the 4 rows
+//     land on 4 different chunk blocks;
+//   - transpose reads of the 16-row kernel, 8 rows x a pair of chunks: bits
+//     1-3 (D = 128), or bits 1-2 across rows of one parity (D = 64), take
+//     distinct values on each aligned group of 8 rows.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
-  if constexpr (D == 128) return r2 | (r0 << 1) | (r1 << 2) | (r3 << 3);
-  else return r2 | ((r0 ^ r3) << 1) | ((r1 ^ r2) << 2);
+  if constexpr (D == 128) return r3 | (r2 << 1) | (r0 << 2) | (r1 << 3);
+  else return r3 | (r2 << 1) | (r1 << 2);
 }
 
 // 16-byte sources for direct loads of rows that are not in the pool: zeros
