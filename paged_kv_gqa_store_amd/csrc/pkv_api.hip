@@ -33,10 +33,10 @@ int copy_unit(std::initializer_list<uint64_t> vals) {
 }
 
 constexpr int kMaxSplits = 1024;
-// (sequence, split) pairs the decode kernels rank longest first.  Every
-// workgroup ranks all of them (n^2 / 256 key comparisons per thread): at 512
-// pairs (the ragged batch at 8 splits) that cost more than the finer split
-// saved (251 against 194 us), at 1024 it took the launch to 856 us.
+// (sequence, split) pairs the decode kernels rank longest first: every
+// workgroup ranks all of them, one pair per thread of its 256.  (With a rank
+// taken by comparing every pair's key with every other, 512 pairs, the ragged
+// batch at 8 splits, cost more than the finer split saved: 251 against 194 us.)
 constexpr int64_t kMaxRankedPairs = 256;
 
 

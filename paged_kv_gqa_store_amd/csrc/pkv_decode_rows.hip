@@ -81,10 +81,9 @@ __global__ __launch_bounds__(256) void paged_decode_rows_kernel(DecodeParams p) 
   int b, s;
   bool empty_pair = false;
   if (p.longest_first) {
-    __shared__ __attribute__((aligned(16))) unsigned sm_key[4 * kWaves * 64];
-    __shared__ int sm_pick;
+    __shared__ __attribute__((aligned(16))) unsigned sm_key[kWaves * 64 + 16];
     const int2 pk = pick_longest_first(p.seq_lens, p.B, p.num_splits, p.chunk, p.max_pages << p.page_log2,
-                                       blockIdx.x / nhb, sm_key, &sm_pick);
+                                       blockIdx.x / nhb, sm_key);
     b = pk.x % p.B;
     s = pk.x / p.B;
     empty_pair = pk.y == 0;

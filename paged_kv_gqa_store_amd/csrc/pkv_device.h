@@ -44,48 +44,78 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Longest-first order of the (sequence, split) pairs of a decode launch: the
 // workgroups of pair rank r (r-th longest; equal lengths in index order) come
-// r-th in the grid.  Every workgroup ranks all n <= 4 * blockDim.x pairs
-// (thread i the pairs i, i + blockDim.x, ...) in LDS and returns the pair
-// whose rank is `target` (pair index i = b + B * s) and its length.  Key of
-// pair i: length * 2048 + (2047 - i) (unique, ordered as length then lower
-// index; lengths < 2^21, checked on the host), compared four at a time;
-// padding keys are 0, below every pair's.
-// sm_key: 4 * blockDim.x unsigned, 16-byte aligned.
+// r-th in the grid.  Every workgroup ranks the n <= blockDim.x pairs (thread i
+// holds pair i = b + B * s; the host caps n) and returns the pair of rank
+// `target` and its length.
+//
+// A pair is full (length = chunk), partial (0 < length < chunk: at most one
+// per sequence, the split holding its last position) or empty.  In the order
+// above, the full pairs come first, in index order, then the partial pairs by
+// key length * 2048 + (2047 - i) (unique, length then lower index), then the
+// empty pairs in index order.  A ballot per class and the per-wave counts
+// give every full and empty pair its rank directly; a partial pair counts the
+// partial keys above its own, compacted in LDS (at most B of them, read four
+// at a time, zero-padded: every key is above zero).
+// sm: blockDim.x + 16 unsigned, 16-byte aligned.
 __device__ __forceinline__ int2 pick_longest_first(const int32_t *seq_lens, int B, int num_splits,
-                                                   int chunk, int max_len, int target,
-                                                   unsigned *sm_key, int *sm_pick) {
+                                                   int chunk, int max_len, int target, unsigned *sm) {
   const int n = B * num_splits;
-  const int nt = blockDim.x;
-  unsigned key[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = threadIdx.x + u * nt;
-    key[u] = 0u;
-    if (i < n) {
-      const int Li = min(max(seq_lens[i % B], 0), max_len);
-      const int len = max(0, min(chunk, Li - (i / B) * chunk));
-      key[u] = unsigned(len) * 2048u + unsigned(2047 - i);
-    }
-    sm_key[i] = key[u];
+  const int nt = blockDim.x, nw = nt / 64;
+  const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
+  unsigned *cnt = sm + nt;        // [wave][class]: full, partial, empty (at most 4 waves)
+  unsigned *res = sm + nt + 12;   // the pick and its length
+  int len = 0, cls = 3;           // class 3: no pair
+  if (i < n) {
+    const int Li = min(max(seq_lens[i % B], 0), max_len);
+    len = max(0, min(chunk, Li - (i / B) * chunk));
+    cls = len == chunk ? 0 : (len > 0 ? 1 : 2);
+  }
+  const unsigned long long bf = __ballot(cls == 0), bp = __ballot(cls == 1), be = __ballot(cls == 2);
+  const unsigned long long mine = cls == 0 ? bf : (cls == 1 ? bp : be);
+  const int below = int(__builtin_amdgcn_mbcnt_hi(unsigned(mine >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(unsigned(mine), 0u)));
+  if (lane == 0) {
+    cnt[3 * wave] = unsigned(__popcll(bf));
+    cnt[3 * wave + 1] = unsigned(__popcll(bp));
+    cnt[3 * wave + 2] = unsigned(__popcll(be));
+  }
+  if (i == 0) {   // a valid pair even if no thread matched (cannot happen with n <= blockDim.x)
+    res[0] = unsigned(min(target, n - 1));
+    res[1] = 0u;
   }
   __syncthreads();
-  const int nq = (n + 3) / 4;
-  const uint4 *k4 = reinterpret_cast<const uint4 *>(sm_key);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = threadIdx.x + u * nt;
-    if (i < n) {
-      int r = 0;
-      for (int j = 0; j < nq; ++j) {
-        const uint4 k = k4[j];
-        r += (k.x > key[u]) + (k.y > key[u]) + (k.z > key[u]) + (k.w > key[u]);
+  int nF = 0, nP = 0, off = 0;
+  for (int w = 0; w < nw; ++w) {
+    nF += int(cnt[3 * w]);
+    nP += int(cnt[3 * w + 1]);
+    if (w < wave && cls < 3) off += int(cnt[3 * w + cls]);
+  }
+  const int idx = off + below;    // position within the pair's class, in index order
+  const unsigned key = unsigned(len) * 2048u + unsigned(2047 - i);
+  if (cls == 1) sm[idx] = key;
+  if (i < 3 && nP + i < ((nP + 3) & ~3)) sm[nP + i] = 0u;
+  __syncthreads();
+  if (cls < 3) {
+    int r;
+    if (cls == 0) {
+      r = idx;
+    } else if (cls == 2) {
+      r = nF + nP + idx;
+    } else {
+      r = nF;
+      const uint4 *k4 = reinterpret_cast<const uint4 *>(sm);
+      for (int q = 0; q < (nP + 3) / 4; ++q) {
+        const uint4 k = k4[q];
+        r += (k.x > key) + (k.y > key) + (k.z > key) + (k.w > key);
       }
-      if (r == target) *sm_pick = i;
+    }
+    if (r == target) {
+      res[0] = unsigned(i);
+      res[1] = unsigned(len);
     }
   }
   __syncthreads();
-  const int pick = *sm_pick;
-  return make_int2(pick, int(sm_key[pick] >> 11));
+  return make_int2(int(res[0]), int(res[1]));
 }
 
 }  // namespace pkv
