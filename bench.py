@@ -60,9 +60,9 @@ ALL_WORKLOADS = ["tiny_gqa", "llama3_8b_decode", "ragged_batch", "long_context",
 # any edit to them voids the figure (then `traffic` is null).
 COUNTED_TRAFFIC = {
     "workload": HEADLINE,
-    "sources_sha256": "7c4aac042feaa3d55e1fef0b8e62af50b10de1071894e65817432cb0fc7294bc",
-    "read_bytes": 1153967326,    # FETCH_SIZE 563483.5 KiB x (1 GiB / 524309.3 KiB)
-    "write_bytes": 4237926,      # WRITE_SIZE 4138.6 KiB x (1 GiB / 1048576.0 KiB)
+    "sources_sha256": "e0562b434d9f2ba4a11496f6b8bbb083d6e29da74599f2f77a600cc2e3adbec9",
+    "read_bytes": 1153926279,    # FETCH_SIZE 563468.4 KiB x (1 GiB / 524313.9 KiB)
+    "write_bytes": 4238131,      # WRITE_SIZE 4138.8 KiB x (1 GiB / 1048576.0 KiB)
 }
 KERNEL_SOURCES = ["pkv_decode_mfma.hip", "pkv_device.h", "pkv_launch.h"]
 
