@@ -77,7 +77,9 @@ PIN_CALLS = [
     (pins.test_indexing_matches_torch_embedding, ()),
     (pins.test_indexing_shards_sum_to_the_full_lookup, ()),
     (pins.test_indexing_closed_forms, ()),
-] + [(pins.test_attention_matches_torch_sdpa_fp64, (c,)) for c in range(4)]
+    (pins.test_prefill_matches_python_loops, ()),
+] + [(pins.test_attention_matches_torch_sdpa_fp64, (c,)) for c in range(4)] + [
+    (pins.test_attention_matches_python_loops, (c,)) for c in (0, 2, 3)]
 
 
 @pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])

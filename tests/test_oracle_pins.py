@@ -132,6 +132,63 @@ def test_attention_matches_torch_sdpa_fp64(case):
         np.testing.assert_allclose(lse[b], torch.logsumexp(scores, dim=-1).numpy(), rtol=1e-14, atol=1e-12)
 
 
+def _brute_attention(q_rows, K, V, page_row, L, P, g, D, last_pos=None):
+    """The definition written out in plain Python loops, one q head at a time:
+    q_rows are the query vectors (lists of floats), K and V nested lists
+    [page][slot][kv head][dim], page_row the sequence's page ids.  Query i
+    sees positions 0 .. last_pos[i] (all L when last_pos is None).  Returns
+    (outputs, lse values)."""
+    outs, lses = [], []
+    for i, qv in enumerate(q_rows):
+        n = L if last_pos is None else last_pos[i] + 1
+        s = []
+        for t in range(n):
+            k = K[page_row[t // P]][t % P][g]
+            s.append(sum(qv[d] * k[d] for d in range(D)) / math.sqrt(D))
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = math.fsum(w)
+        o = [math.fsum(w[t] * V[page_row[t // P]][t % P][g][d] for t in range(n)) / z for d in range(D)]
+        outs.append(o)
+        lses.append(m + math.log(z))
+    return outs, lses
+
+
+@pytest.mark.parametrize("case", [0, 2, 3])
+def test_attention_matches_python_loops(case):
+    """Brute force on tiny inputs: the plain loops above, independent of both
+    the C oracle and torch, for every (sequence, q head)."""
+    cfg, _ = list(small_cases())[case]
+    inp = W.make_inputs(cfg)
+    kf, vf = _after_store(inp)
+    out, lse = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    G = cfg.Hq // cfg.Hkv
+    K, V, Q = _f64(kf).tolist(), _f64(vf).tolist(), _f64(inp.q).tolist()
+    for b in range(cfg.B):
+        L = int(inp.seq_lens[b])
+        row = [int(x) for x in inp.page_table[b]]
+        for h in range(cfg.Hq):
+            (o,), (l,) = _brute_attention([Q[b][h]], K, V, row, L, cfg.P, h // G, cfg.D)
+            np.testing.assert_allclose(out[b, h], o, rtol=0, atol=1e-12)
+            assert abs(lse[b, h] - l) <= 1e-12 * max(1.0, abs(l))
+
+
+def test_prefill_matches_python_loops():
+    """The causal prefill against the same loops: request b's query row j sits
+    at position kv_len - q_len + j and sees positions up to it."""
+    q_lens, kv_lens = (3, 1, 6), (5, 9, 6)
+    q, kp, vp, pt, kl, qo = _prefill_case(q_lens, kv_lens, Hq=4, Hkv=2, D=16, P=4)
+    out, lse = oracle.paged_prefill(q, kp, vp, pt, kl, qo, True)
+    K, V, Q = _f64(kp).tolist(), _f64(vp).tolist(), _f64(q).tolist()
+    for b, (ql, L) in enumerate(zip(q_lens, kv_lens)):
+        row = [int(x) for x in pt[b]]
+        for h in range(4):
+            rows = [Q[qo[b] + j][h] for j in range(ql)]
+            o, l = _brute_attention(rows, K, V, row, L, 4, h // 2, 16, [L - ql + j for j in range(ql)])
+            np.testing.assert_allclose(out[qo[b]:qo[b + 1], h], o, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[qo[b]:qo[b + 1], h], l, rtol=1e-13, atol=1e-12)
+
+
 def test_softmax_weights_sum_to_one():
     inp = W.make_inputs(W.WORKLOADS["tiny_gqa"])
     kf, vf = _after_store(inp)
