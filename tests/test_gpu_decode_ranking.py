@@ -68,3 +68,26 @@ def test_ranking_edges(gpu_device, kind, B, S, G, D):
     check_attention(out, ref, f"ranking edge {kind} B{B} S{S}")
     a, b = host_f64_from_bf16(out), host_f64_from_bf16(one)
     assert (np.abs(a - b) <= np.abs(b) * 2.0 ** -7 + 1e-6).all(), "S splits and one split differ by more than one bf16 step"
+
+
+@pytest.mark.parametrize("G,D", [(4, 128), (1, 64)])
+def test_large_batch(gpu_device, G, D):
+    """4096 sequences of 0-48 tokens (some empty): a grid of 4096 x Hkv x S
+    workgroups in launch order (far past the ranking limit), on the
+    matrix-core kernel (G = 4) and the row kernel (G = 1)."""
+    rng = np.random.Generator(np.random.PCG64(W.SEED_BASE + 7600 + G))
+    B, P = 4096, 16
+    lens = rng.integers(0, 49, B)
+    lens[0] = 48
+    Hkv = 8
+    cfg = W.custom_config(seed_id=7600 + G, name=f"large_batch_g{G}", B=B, Hq=G * Hkv, Hkv=Hkv, D=D, P=P,
+                          num_pages=int((-(-lens // P)).sum()) + 8, seq_lens=tuple(int(x) for x in lens))
+    inp = W.make_inputs(cfg)
+    print(f"large batch: {cfg.describe()}", flush=True)
+    kf, vf = inp.pools_after_store()
+    ref, _ = oracle.paged_decode(inp.q, kf, vf, inp.page_table, inp.seq_lens)
+    for S in (1, 3):
+        st = DeviceStep(inp, gpu_device)
+        out, _, _ = st.step(splits=S)
+        torch.cuda.synchronize()
+        check_attention(out, ref, f"large batch G{G} S{S}")
