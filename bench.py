@@ -60,9 +60,9 @@ ALL_WORKLOADS = ["tiny_gqa", "llama3_8b_decode", "ragged_batch", "long_context",
 # any edit to them voids the figure (then `traffic` is null).
 COUNTED_TRAFFIC = {
     "workload": HEADLINE,
-    "sources_sha256": "e0562b434d9f2ba4a11496f6b8bbb083d6e29da74599f2f77a600cc2e3adbec9",
-    "read_bytes": 1153926279,    # FETCH_SIZE 563468.4 KiB x (1 GiB / 524313.9 KiB)
-    "write_bytes": 4238131,      # WRITE_SIZE 4138.8 KiB x (1 GiB / 1048576.0 KiB)
+    "sources_sha256": "714e7776efbba3b64a3767dbcb358b891e1386061080161832643780d5a5409a",
+    "read_bytes": 1153932570,    # FETCH_SIZE 563469.0 KiB x (1 GiB / 524311.6 KiB)
+    "write_bytes": 4238950,      # WRITE_SIZE 4139.6 KiB x (1 GiB / 1048576.0 KiB)
 }
 KERNEL_SOURCES = ["pkv_decode_mfma.hip", "pkv_device.h", "pkv_launch.h"]
 

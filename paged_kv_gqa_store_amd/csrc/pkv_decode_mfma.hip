@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kWaves * 64) void paged_decode_mfma_kernel(DecodePa
   int g = blockIdx.x % p.Hkv, b, s;
   bool empty_pair = false;        // a split past its sequence's end (known in the longest-first order)
   if (p.longest_first) {
-    __shared__ __attribute__((aligned(16))) unsigned sm_key[kWaves * 64 + 16];
+    __shared__ __attribute__((aligned(16))) unsigned sm_key[kRankScratch<kWaves>];
     const int2 pk = pick_longest_first(p.seq_lens, p.B, p.num_splits, p.chunk, p.max_pages << p.page_log2,
                                        blockIdx.x / p.Hkv, sm_key);
     b = pk.x % p.B;

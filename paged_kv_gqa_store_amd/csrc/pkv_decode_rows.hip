@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void paged_decode_rows_kernel(DecodeParams p) 
   int b, s;
   bool empty_pair = false;
   if (p.longest_first) {
-    __shared__ __attribute__((aligned(16))) unsigned sm_key[kWaves * 64 + 16];
+    __shared__ __attribute__((aligned(16))) unsigned sm_key[kRankScratch<kWaves>];
     const int2 pk = pick_longest_first(p.seq_lens, p.B, p.num_splits, p.chunk, p.max_pages << p.page_log2,
                                        blockIdx.x / nhb, sm_key);
     b = pk.x % p.B;

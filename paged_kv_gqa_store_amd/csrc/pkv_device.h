@@ -56,14 +56,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // give every full and empty pair its rank directly; a partial pair counts the
 // partial keys above its own, compacted in LDS (at most B of them, read four
 // at a time, zero-padded: every key is above zero).
-// sm: blockDim.x + 16 unsigned, 16-byte aligned.
+// sm: blockDim.x + 3 * (waves) + 2 unsigned, 16-byte aligned (kRankScratch).
+template <int kWaves>
+constexpr int kRankScratch = kWaves * 64 + 3 * kWaves + 2;
+
 __device__ __forceinline__ int2 pick_longest_first(const int32_t *seq_lens, int B, int num_splits,
                                                    int chunk, int max_len, int target, unsigned *sm) {
   const int n = B * num_splits;
   const int nt = blockDim.x, nw = nt / 64;
   const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
-  unsigned *cnt = sm + nt;        // [wave][class]: full, partial, empty (at most 4 waves)
-  unsigned *res = sm + nt + 12;   // the pick and its length
+  unsigned *cnt = sm + nt;            // [wave][class]: full, partial, empty
+  unsigned *res = sm + nt + 3 * nw;   // the pick and its length
   int len = 0, cls = 3;           // class 3: no pair
   if (i < n) {
     const int Li = min(max(seq_lens[i % B], 0), max_len);
