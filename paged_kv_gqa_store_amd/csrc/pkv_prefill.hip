@@ -120,23 +120,39 @@ struct Slice {
 // so id i takes logical slot (i % 8) * (n / 8) + i / 8 and each XCD runs a
 // contiguous slice of the logical order (kv-head group major, then q chunks),
 // whose workgroups read the same K/V rows through one L2.  The q chunks run
-// last-first: with the causal mask they are the longest.
+// last-first: with the causal mask they are the longest.  The n % 8 slots
+// past the slices keep their ids.
+__device__ __forceinline__ int xcd_slot(unsigned lin, unsigned n) {
+  const unsigned per_xcd = n / 8;
+  return int(lin < 8 * per_xcd ? (lin % 8) * per_xcd + lin / 8 : lin);
+}
+
+// Two jobs per workgroup: workgroup i of XCD i % 8 takes slots j and
+// per_xcd - 1 - j of that XCD's slice, j = i / 8: the j-th longest q chunk and
+// the j-th shortest, so every workgroup of the XCD gets about the same work,
+// and the second job's loads and products hide the first job's prologue and
+// the drain of its output stores (a workgroup of 8 waves fills its CU, so
+// no other workgroup can).  An odd slice's middle slot runs once; the n % 8
+// slots past the slices get a workgroup each.  -1: no such job.
+__device__ __forceinline__ int paired_slot(unsigned lin, unsigned n, int job) {
+  const unsigned per_xcd = n / 8, half = (per_xcd + 1) / 2;
+  if (lin >= 8 * half) return job == 0 ? int(8 * per_xcd + (lin - 8 * half)) : -1;
+  const unsigned x = lin % 8, j = lin / 8;
+  const unsigned s = job == 0 ? j : per_xcd - 1 - j;
+  if (job == 1 && s == j) return -1;
+  return int(x * per_xcd + s);
+}
+__host__ __device__ constexpr unsigned paired_grid(unsigned n) { return 8 * ((n / 8 + 1) / 2) + n % 8; }
+
+// The job at logical slot `logical` (one of the orders above).
 //
-// With RW = 128 rows a workgroup's slot is a pair of consecutive host tiles,
-// 2x and 2x + 1.  When both belong to one request (consecutive tile indices)
-// they are one job of up to 128 rows; otherwise (a request boundary, or the
-// last tile alone) each tile is a job of its own, run one after the other.
-// Returns false when the workgroup has no job number `job`.
 template <int HB, int RW>
-__device__ __forceinline__ bool locate(const PrefillParams &p, Slice &w, int job) {
+__device__ __forceinline__ bool locate(const PrefillParams &p, Slice &w, int job, int logical) {
   constexpr int CH = RW < kQTile ? kQTile / RW : 1;   // workgroups along one host tile
   constexpr int TPW = RW > kQTile ? RW / kQTile : 1;  // host tiles per workgroup
   static_assert(TPW <= 2, "at most a pair of host tiles per workgroup");
   const int hgroups = (p.G + HB - 1) / HB;
   const int n_x = (p.num_q_tiles + TPW - 1) / TPW * CH;   // workgroups per group
-  const unsigned nwg = gridDim.x, per_xcd = nwg / 8;
-  const unsigned lin = blockIdx.x;
-  const int logical = int(lin < 8 * per_xcd ? (lin % 8) * per_xcd + lin / 8 : lin);
   // With long requests, the GB = groups / 8 groups of one XCD interleave
   // their q chunks inside the XCD's slice, so that the XCD starts every
   // group's longest chunks first rather than one group's after another's.
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void paged_prefill16_kernel(PrefillParams
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Slice w;
-  if (!locate<1, kQTile>(p, w, 0)) return;
+  if (!locate<1, kQTile>(p, w, 0, xcd_slot(blockIdx.x, gridDim.x))) return;
   const int h = w.g * p.G + w.hg;            // G == 1: the kv head's only q head
   const int my_row = w.wg_row0 + 16 * wave + (lane & 15);
   const bool row_ok = my_row < w.q_len;
@@ -471,11 +487,17 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // one job, or two for a pair of host tiles that does not continue one request
+  // one job; or two for a pair of host tiles that does not continue one
+  // request; or with 8 waves the two mirrored slots of paired_slot
   constexpr int TPW = RW > kQTile ? RW / kQTile : 1;
-  for (int job = 0; job < TPW; ++job) {
+  constexpr bool kPaired = W == 8 && TPW == 1;
+  constexpr int NJ = kPaired ? 2 : TPW;
+  constexpr int CH = RW < kQTile ? kQTile / RW : 1;
+  const unsigned n_slots = unsigned((p.num_q_tiles + TPW - 1) / TPW * CH * p.Hkv * ((p.G + HB - 1) / HB));
+  for (int job = 0; job < NJ; ++job) {
     Slice w;
-    if (!locate<HB, RW>(p, w, job)) continue;
+    const int slot = kPaired ? paired_slot(blockIdx.x, n_slots, job) : xcd_slot(blockIdx.x, gridDim.x);
+    if (slot < 0 || !locate<HB, RW>(p, w, kPaired ? 0 : job, slot)) continue;
     if (job > 0) __syncthreads();            // every wave is done with the previous job's tiles
     const int h_in_group = w.hg * HB + wave / WPH;
     const bool head_ok = h_in_group < p.G;
@@ -648,7 +670,8 @@ hipError_t launch32(const PrefillParams &p, hipStream_t stream) {
   constexpr int CH = RW < kQTile ? kQTile / RW : 1;
   constexpr int TPW = RW > kQTile ? RW / kQTile : 1;
   const int hgroups = (p.G + HB - 1) / HB;
-  const dim3 grid{unsigned((p.num_q_tiles + TPW - 1) / TPW * CH * p.Hkv * hgroups)}, block{W * 64};
+  const unsigned n_slots = unsigned((p.num_q_tiles + TPW - 1) / TPW * CH * p.Hkv * hgroups);
+  const dim3 grid{W == 8 && TPW == 1 ? paired_grid(n_slots) : n_slots}, block{W * 64};
   hipLaunchKernelGGL((paged_prefill32_kernel<D, HB, W>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
